@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of one VMoBA attention layer, forward + backward, on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input already resident in
+HBM: block-mean pooling -> global threshold selection -> block-sparse attention
+forward -> backward (delta, dK/dV, dQ).  The default workload is the 3D layer at the
+93x576x1024 training length: latent 24x36x64 = 55,296 tokens, 12 heads of 128, blocks
+(4, 6, 8), tau = 0.25.
+
+Prints one JSON line.  value = algorithmic TFLOP/s over the selected pairs,
+(4 + 8) * d * P per step with P the selected token pairs (forward: Q K^T and P V;
+backward: dV, dP, dQ, dK), divided by the measured step time.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="l3d_55k")
+    ap.add_argument("--layer", type=int, default=0, help="layer of the workload's cycle")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, cfg, spec, tau):
+    """The fp64 oracle on the host cores, on one head of the same layer."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info())
+    except Exception:
+        threads = os.cpu_count()
+    q, k, v, do = (inp[x][:, :, :1].float().numpy() for x in ("q", "k", "v", "do"))
+    T, H, W = cfg["T"], cfg["H"], cfg["W"]
+    t0 = time.perf_counter()
+    mem = oracle.block_members(T, H, W, spec.block)
+    qp, kp = oracle.block_means(q, mem), oracle.block_means(k, mem)
+    mask, _, _ = oracle.select_all_heads(qp, kp, tau)
+    o, lse = oracle.sparse_attention_fwd(q, k, v, mem, mask)
+    oracle.sparse_attention_bwd(q, k, v, o, lse, do, mem, mask)
+    dt = time.perf_counter() - t0
+    S = mem.shape[1]
+    pairs = float(mask.sum()) * S * S
+    flops = 12.0 * cfg["head_dim"] * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"head 0 of 12 of the same layer (pool, select, sparse fwd+bwd in "
+                      f"fp64), {dt:.1f} s wall, {flops / 1e12:.3f} TFLOP algorithmic",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the layer "
+              f"would shard over heads, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synthetic import CONFIGS, make_layer_inputs
+    import block_sparse_attention_layer_amd as vm
+
+    cfg = CONFIGS[args.workload]
+    spec = cfg["layers"][args.layer]
+    tau = args.tau if args.tau is not None else (0.25 if 0.25 in cfg["taus"] else cfg["taus"][0])
+    dev = torch.device("cuda:0")
+    inp = make_layer_inputs(args.workload, args.layer, backward=True)
+    dtype = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    p = vm.Problem(cfg["batch"], cfg["heads"], cfg["head_dim"], cfg["T"], cfg["H"], cfg["W"],
+                   spec.layer_idx, tuple(spec.block), dtype, dtype)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    nb = vm.vmoba_num_blocks(p)
+    S = p.L // nb
+    d = p.head_dim
+
+    names = ["pool", "select", "fwd", "delta", "dkdv", "dq"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        qp, kp = vm.vmoba_partition_pool(p, q, k)
+        mark(1)
+        sel = vm.vmoba_select(p, qp, kp, tau)
+        mark(2)
+        o, lse = vm.vmoba_sparse_attn_fwd(p, q, k, v, sel.row_ptr, sel.col_idx)
+        mark(3)
+        delta = vm.vmoba_sparse_attn_bwd_delta(p, o, do)
+        mark(4)
+        dk, dv = vm.vmoba_sparse_attn_bwd_dkdv(p, q, k, v, lse, delta, do, sel.col_ptr,
+                                               sel.row_idx)
+        mark(5)
+        dq = vm.vmoba_sparse_attn_bwd_dq(p, q, k, v, lse, delta, do, sel.row_ptr,
+                                         sel.col_idx)
+        mark(6)
+        return sel
+
+    for _ in range(args.warmup):
+        sel = step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sel = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                for j, n in enumerate(names)}
+
+    nnz = float(sel.head_stats[:, 1].double().sum().item())
+    pairs = nnz * S * S
+    density = nnz / (p.groups * nb * nb)
+    fl = {"fwd": 4.0 * d * pairs, "dkdv": 6.0 * d * pairs, "dq": 2.0 * d * pairs}
+    executed = {"fwd": 4.0 * d * pairs, "dkdv": 8.0 * d * pairs, "dq": 6.0 * d * pairs}
+    total_flops = 12.0 * d * pairs
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    attn = ["fwd", "dkdv", "dq"]
+    dom = max(attn, key=lambda n: stage_ms[n])
+    achieved = fl[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    esz = 2 if dtype == torch.bfloat16 else 4
+    pool_bytes = 2.0 * p.L * p.groups * d * esz + 2.0 * p.groups * nb * d * 4
+    select_bytes = 2.0 * p.groups * nb * d * 4 + 6.0 * p.groups * nb * nb * 4
+    kernel_names = {"fwd": "attn_fwd_bf16_kernel", "dkdv": "attn_bwd_dkdv_bf16_kernel",
+                    "dq": "attn_bwd_dq_bf16_kernel"}
+
+    dense = None
+    if not args.no_dense:
+        o_d, lse_d = vm.vmoba_dense_attn_fwd(p, q, k, v)
+        vm.vmoba_dense_attn_bwd(p, q, k, v, o_d, lse_d, do)
+        torch.cuda.synchronize()
+        reps = 2
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            o_d, lse_d = vm.vmoba_dense_attn_fwd(p, q, k, v)
+            vm.vmoba_dense_attn_bwd(p, q, k, v, o_d, lse_d, do)
+        torch.cuda.synchronize()
+        dense = (time.perf_counter() - t1) * 1e3 / reps
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, cfg, spec, tau)
+        cpu.pop("seconds")
+
+    line = {
+        "metric": "VMoBA attn fwd+bwd ms/layer & TFLOP/s (% bf16 MFMA peak) at 55K tokens",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: layer_idx {spec.layer_idx} (l mod 3 = "
+                        f"{spec.layer_idx % 3}), latent {p.T}x{p.H}x{p.W} = {p.L} tokens, "
+                        f"{p.heads} heads x {d}, blocks {tuple(spec.block)} ({nb} blocks of "
+                        f"{S}), tau {tau}, pool+select+sparse fwd+bwd",
+            "global_batch": p.batch, "seq_len": p.L, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "kernel": kernel_names[dom], "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "avg_ms": round(stage_ms[dom], 4),
+            "algorithmic_flops_per_launch": fl[dom],
+            "executed_flops_per_launch": executed[dom]},
+        "cpu_baseline": cpu,
+        "stages_ms": {n: round(stage_ms[n], 4) for n in names},
+        "stage_tflops": {n: round(fl[n] / (stage_ms[n] * 1e-3) / 1e12, 2) for n in attn},
+        "stage_frac_bf16_peak": {n: round(fl[n] / (stage_ms[n] * 1e-3) / 1e12 /
+                                          PEAK_BF16_TFLOPS, 4) for n in attn},
+        "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
+        "pool_frac_hbm": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "select_gbs": round(select_bytes / (stage_ms["select"] * 1e-3) / 1e9, 1),
+        "select_frac_hbm": round(select_bytes / (stage_ms["select"] * 1e-3) / 1e9 /
+                                 PEAK_HBM_GBS, 5),
+        "kept_pair_density": round(density, 5),
+        "selected_token_pairs": pairs,
+        "dense_ms_per_step": None if dense is None else round(dense, 3),
+        "speedup_vs_dense": None if dense is None else round(dense / ms_step, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+// Entry points of the C ABI declared in include/vmoba.h: host-side argument checks,
+// then the kernel launchers.  Nothing is enqueued when a check fails.
+#include <math.h>
+
+#include "../../include/vmoba.h"
+#include "internal.h"
+
+using namespace vmoba;
+
+namespace {
+
+int check_common(const vmoba_problem* p) { return validate_problem(p); }
+
+int check_blocks(const vmoba_problem* p) {
+  const Geom g = make_geom(p);
+  return g.Nb <= kMaxBlocks ? VMOBA_OK : VMOBA_ERR_SHAPE;
+}
+
+int check_ws(const vmoba_problem* p, int op, const void* ws, size_t ws_bytes) {
+  size_t need = 0;
+  int st = workspace_bytes(p, op, &need);
+  if (st) return st;
+  if (need > ws_bytes) return VMOBA_ERR_WORKSPACE;
+  if (need > 0 && !ws) return VMOBA_ERR_NULL;
+  return VMOBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vmoba_partition_pool(const vmoba_problem* p, const void* q, const void* k,
+                         float* q_pool, float* k_pool, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if (!q || !k || !q_pool || !k_pool) return VMOBA_ERR_NULL;
+  return launch_pool(make_geom(p), q, k, q_pool, k_pool, stream);
+}
+
+int vmoba_select(const vmoba_problem* p, const float* q_pool, const float* k_pool,
+                 float tau, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
+                 int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
+                 size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  if (!(tau > 0.0f) || !(tau <= 1.0f) || !isfinite(tau)) return VMOBA_ERR_TAU;
+  if (!q_pool || !k_pool || !row_ptr || !col_idx || !col_ptr || !row_idx || !head_stats)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_SELECT, ws, ws_bytes))) return st;
+  return launch_select(make_geom(p), q_pool, k_pool, tau, row_ptr, col_idx, col_ptr,
+                       row_idx, head_stats, norm_scores, ws, stream);
+}
+
+int vmoba_sparse_attn_fwd(const vmoba_problem* p, const void* q, const void* k,
+                          const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                          void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  if (!q || !k || !v || !row_ptr || !col_idx || !o || !lse) return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_SPARSE_FWD, ws, ws_bytes))) return st;
+  return launch_attn_fwd(make_geom(p), false, q, k, v, row_ptr, col_idx, o, lse, ws,
+                         stream);
+}
+
+int vmoba_sparse_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
+                          const void* v, const void* o, const float* lse,
+                          const void* dout, const int32_t* row_ptr,
+                          const int32_t* col_idx, const int32_t* col_ptr,
+                          const int32_t* row_idx, void* dq, void* dk, void* dv, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !row_ptr || !col_idx || !col_ptr ||
+      !row_idx || !dq || !dk || !dv)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_SPARSE_BWD, ws, ws_bytes))) return st;
+  const Geom g = make_geom(p);
+  float* delta = static_cast<float*>(ws);
+  if ((st = launch_bwd_delta(g, o, dout, delta, stream))) return st;
+  if ((st = launch_bwd_dkdv(g, false, q, k, v, lse, delta, dout, col_ptr, row_idx, dk, dv,
+                            stream)))
+    return st;
+  return launch_bwd_dq(g, false, q, k, v, lse, delta, dout, row_ptr, col_idx, dq, stream);
+}
+
+int vmoba_sparse_attn_bwd_delta(const vmoba_problem* p, const void* o, const void* dout,
+                                float* delta, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if (!o || !dout || !delta) return VMOBA_ERR_NULL;
+  return launch_bwd_delta(make_geom(p), o, dout, delta, stream);
+}
+
+int vmoba_sparse_attn_bwd_dkdv(const vmoba_problem* p, const void* q, const void* k,
+                               const void* v, const float* lse, const float* delta,
+                               const void* dout, const int32_t* col_ptr,
+                               const int32_t* row_idx, void* dk, void* dv, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  if (!q || !k || !v || !lse || !delta || !dout || !col_ptr || !row_idx || !dk || !dv)
+    return VMOBA_ERR_NULL;
+  return launch_bwd_dkdv(make_geom(p), false, q, k, v, lse, delta, dout, col_ptr, row_idx,
+                         dk, dv, stream);
+}
+
+int vmoba_sparse_attn_bwd_dq(const vmoba_problem* p, const void* q, const void* k,
+                             const void* v, const float* lse, const float* delta,
+                             const void* dout, const int32_t* row_ptr,
+                             const int32_t* col_idx, void* dq, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  if (!q || !k || !v || !lse || !delta || !dout || !row_ptr || !col_idx || !dq)
+    return VMOBA_ERR_NULL;
+  return launch_bwd_dq(make_geom(p), false, q, k, v, lse, delta, dout, row_ptr, col_idx, dq,
+                       stream);
+}
+
+int vmoba_dense_attn_fwd(const vmoba_problem* p, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if (!q || !k || !v || !o || !lse) return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_DENSE_FWD, ws, ws_bytes))) return st;
+  return launch_attn_fwd(make_geom(p), true, q, k, v, nullptr, nullptr, o, lse, ws,
+                         stream);
+}
+
+int vmoba_dense_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_DENSE_BWD, ws, ws_bytes))) return st;
+  const Geom g = make_geom(p);
+  float* delta = static_cast<float*>(ws);
+  if ((st = launch_bwd_delta(g, o, dout, delta, stream))) return st;
+  if ((st = launch_bwd_dkdv(g, true, q, k, v, lse, delta, dout, nullptr, nullptr, dk, dv,
+                            stream)))
+    return st;
+  return launch_bwd_dq(g, true, q, k, v, lse, delta, dout, nullptr, nullptr, dq, stream);
+}
+
+}  // extern "C"

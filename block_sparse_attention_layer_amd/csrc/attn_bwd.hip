@@ -1,0 +1,774 @@
+// Block-sparse (and dense) flash attention backward for gfx950, with the block selection
+// held constant (it is not differentiated):
+//   P = exp(q.k/sqrt(d) - lse),  dV = P^T dO,  dP = dO V^T,  delta = rowsum(dO * O),
+//   dS = P * (dP - delta),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
+//
+// Three kernels, no atomics, deterministic:
+//  * delta_kernel: delta per query row (16 lanes per row, shuffle reduction).
+//  * dkdv kernel (key-major, over the column lists): each wave owns 32 keys of one key
+//    block with K and V as register-resident MFMA B operands; the workgroup streams the
+//    query tokens of every query block that selected this key block (tiles of 32 cross
+//    block boundaries), staging Q and dO in LDS both row-major (A operands of S = Q K^T
+//    and dP = dO V^T) and transposed (A operands of dV^T += dO^T P and dK^T += Q^T dS).
+//    S, P, dP and dS live with one key per lane, so P and dS feed the next MFMA straight
+//    from registers; LSE and delta per query come from LDS.
+//  * dq kernel (query-major, over the row lists): the forward's layout (one query per
+//    lane, Q and dO fragments in registers); K and V are staged row-major for
+//    S^T = K Q^T and dP^T = V dO^T, and K once more transposed for dQ^T += K^T dS^T.
+#include <math.h>
+
+#include "attn_common.h"
+
+namespace vmoba {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(Geom g, const T* __restrict__ o,
+                                                    const T* __restrict__ dout,
+                                                    float* __restrict__ delta) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LPR = D / VEC;  // lanes per row
+  const int row = (blockIdx.x * 256 + threadIdx.x) / LPR;  // (b*L + x)*Hh + h
+  const int c = threadIdx.x % LPR;
+  const int nrows = g.B * g.L * g.Hh;
+  float acc = 0.f;
+  if (row < nrows) {
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(o + size_t(row) * D + c * VEC);
+    const u32x4 dv = *reinterpret_cast<const u32x4*>(dout + size_t(row) * D + c * VEC);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += bf16_to_f32(ov[e] & 0xffffu) * bf16_to_f32(dv[e] & 0xffffu);
+        acc += bf16_to_f32(ov[e] >> 16) * bf16_to_f32(dv[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += __uint_as_float(ov[e]) * __uint_as_float(dv[e]);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < nrows && c == 0) {
+    const int h = row % g.Hh;
+    const int bx = row / g.Hh;  // b*L + x
+    const int b = bx / g.L, x = bx - b * g.L;
+    delta[(size_t(b) * g.Hh + h) * g.L + x] = acc;
+  }
+}
+
+// Store four consecutive gradient values as bf16 (round to nearest even) or fp32.
+template <typename GT>
+__device__ __forceinline__ void store4(GT* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(GT) == 2) {
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dK, dV: one wave per 32 keys, query stream from the column list of the key block.
+template <int D, int NW, bool DENSE, typename GT>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
+  constexpr int NT = NW * 64;
+  constexpr int QT = 32;                    // queries per tile
+  constexpr int CH = D / 8;
+  constexpr int QPT = QT * CH / NT;         // queries staged per thread
+  static_assert(QT * CH % NT == 0 && NT % CH == 0 && QPT % 2 == 0, "staging split");
+  constexpr int RSTR = D + 8;               // row-major stride
+  constexpr int TSTR = QT + 4;              // transposed stride
+  constexpr int STAGE = 2 * QT * RSTR + 2 * D * TSTR;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][QT];
+  __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[NW];
+
+  const Geom& g = a.g;
+  const int nrow = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int kt = bid % a.tiles;
+  bid /= a.tiles;
+  const int jblk = bid % nrow;
+  const int grp = bid / nrow;
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
+  GT* __restrict__ dK = static_cast<GT*>(a.dk);
+  GT* __restrict__ dV = static_cast<GT*>(a.dv);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  int nq;
+  if constexpr (DENSE) {
+    nq = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.col_ptr, grp, jblk, &start, &len);
+    nq = compact_list<NT>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, rows_l,
+                          scratch) * g.S;
+  }
+  const int ntiles = (nq + QT - 1) / QT;
+
+  const int klim = DENSE ? g.L : g.S;
+  const int rk = kt * NW * 32 + w * 32 + l32;
+  const bool kvalid = rk < klim;
+  const int rkc = kvalid ? rk : 0;
+  const int32_t xk = DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
+  const int32_t koff = row_offset(g, grp, xk);
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + koff + s * 16 + half * 8));
+    vf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(V + koff + s * 16 + half * 8));
+  }
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      dkacc[dt][v] = 0.f;
+      dvacc[dt][v] = 0.f;
+    }
+
+  const int c = tid % CH, qg = tid / CH;
+  u32x4 qreg[QPT], oreg[QPT];
+  float lse_reg = 0.f, dl_reg = 0.f;
+  const float* lse_g = a.lse + size_t(grp) * g.L;
+  const float* dl_g = a.delta + size_t(grp) * g.L;
+
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int p = t * QT + qg * QPT + u;
+      const bool ok = p < nq;
+      const int pc = ok ? p : 0;
+      const int32_t x = DENSE ? pc : stream_token(g, rows_l, uint32_t(pc));
+      const int32_t off = row_offset(g, grp, x) + c * 8;
+      u32x4 qq = *reinterpret_cast<const u32x4*>(Q + off);
+      u32x4 oo = *reinterpret_cast<const u32x4*>(dO + off);
+      if (!ok) {
+        qq = u32x4{0u, 0u, 0u, 0u};
+        oo = u32x4{0u, 0u, 0u, 0u};
+      }
+      qreg[u] = qq;
+      oreg[u] = oo;
+    }
+    if (tid < QT) {
+      const int p = t * QT + tid;
+      if (p < nq) {
+        const int32_t x = DENSE ? p : stream_token(g, rows_l, uint32_t(p));
+        lse_reg = lse_g[x] * kLog2e;
+        dl_reg = dl_g[x];
+      } else {
+        lse_reg = INFINITY;  // P = 0 for padding queries
+        dl_reg = 0.f;
+      }
+    }
+  };
+  auto transpose_store = [&](uint16_t* dst_base, const u32x4* regs) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t packed[QPT / 2];
+#pragma unroll
+      for (int u = 0; u < QPT; u += 2) {
+        const uint32_t lo = (regs[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (regs[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        packed[u / 2] = lo | (hi << 16);
+      }
+      uint16_t* dst = dst_base + (c * 8 + e) * TSTR + qg * QPT;
+      if constexpr (QPT == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = packed[0];
+      } else {
+        static_assert(QPT == 4, "QPT");
+        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint16_t* Qs = smem + st * STAGE;
+    uint16_t* Os = Qs + QT * RSTR;
+    uint16_t* Qt = Os + QT * RSTR;
+    uint16_t* Ot = Qt + D * TSTR;
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      *reinterpret_cast<u32x4*>(Qs + (qg * QPT + u) * RSTR + c * 8) = qreg[u];
+      *reinterpret_cast<u32x4*>(Os + (qg * QPT + u) * RSTR + c * 8) = oreg[u];
+    }
+    transpose_store(Qt, qreg);
+    transpose_store(Ot, oreg);
+    if (tid < QT) {
+      lse_s[st][tid] = lse_reg;
+      dl_s[st][tid] = dl_reg;
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const uint16_t* Qs = smem + st * STAGE;
+    const uint16_t* Os = Qs + QT * RSTR;
+    const uint16_t* Qt = Os + QT * RSTR;
+    const uint16_t* Ot = Qt + D * TSTR;
+
+    f32x16 sacc, dpacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      sacc[v] = 0.f;
+      dpacc[v] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 qa =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(Qs + l32 * RSTR + s * 16 + half * 8));
+      const bf16x8 oa =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(Os + l32 * RSTR + s * 16 + half * 8));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc, 0, 0, 0);
+    }
+    // sacc[v]: query 8*(v/4) + 4*half + v%4 of the tile, key = this lane
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[st][gq * 8 + half * 4]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[st][gq * 8 + half * 4]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = 4 * gq + r;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[r]));
+        sacc[v] = pv;
+        dpacc[v] = pv * (dpacc[v] - dv4[r]);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int g0 = ks * 8;
+      u32x4 pw, sw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = pack_bf16x2(sacc[g0 + 2 * e], sacc[g0 + 2 * e + 1]);
+        sw[e] = pack_bf16x2(dpacc[g0 + 2 * e], dpacc[g0 + 2 * e + 1]);
+      }
+      const bf16x8 pb = as_bf16x8(pw), sb = as_bf16x8(sw);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int ro = (dt * 32 + l32) * TSTR + ks * 16 + half * 4;
+        const u32x2 olo = *reinterpret_cast<const u32x2*>(Ot + ro);
+        const u32x2 ohi = *reinterpret_cast<const u32x2*>(Ot + ro + 8);
+        const u32x2 qlo = *reinterpret_cast<const u32x2*>(Qt + ro);
+        const u32x2 qhi = *reinterpret_cast<const u32x2*>(Qt + ro + 8);
+        dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]}), pb, dvacc[dt], 0, 0, 0);
+        dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dkacc[dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  if (kvalid) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = dt * 32 + gq * 8 + half * 4;
+        const float sc = a.scale;
+        store4(dK + koff + d0, dkacc[dt][4 * gq] * sc, dkacc[dt][4 * gq + 1] * sc,
+               dkacc[dt][4 * gq + 2] * sc, dkacc[dt][4 * gq + 3] * sc);
+        store4(dV + koff + d0, dvacc[dt][4 * gq], dvacc[dt][4 * gq + 1],
+               dvacc[dt][4 * gq + 2], dvacc[dt][4 * gq + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dQ: one wave per 32 queries, key stream from the row list of the query block.
+template <int D, int NW, int KSUB, bool DENSE, typename GT>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a) {
+  constexpr int NT = NW * 64;
+  constexpr int QT = NW * 32;
+  constexpr int KT = KSUB * 32;
+  constexpr int CH = D / 8;
+  constexpr int KPT = KT * CH / NT;
+  static_assert(KT * CH % NT == 0 && NT % CH == 0 && KPT % 2 == 0, "staging split");
+  constexpr int RSTR = D + 8;
+  constexpr int TSTR = KT + 4;
+  constexpr int STAGE = 2 * KT * RSTR + D * TSTR;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[NW];
+
+  const Geom& g = a.g;
+  const int rows = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int qt = bid % a.tiles;
+  bid /= a.tiles;
+  const int iblk = bid % rows;
+  const int grp = bid / rows;
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
+  GT* __restrict__ dQ = static_cast<GT*>(a.dq);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    nkeys = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, cols,
+                             scratch) * g.S;
+  }
+  const int ntiles = (nkeys + KT - 1) / KT;
+
+  const int qlim = DENSE ? g.L : g.S;
+  const int rq = qt * QT + w * 32 + l32;
+  const bool qvalid = rq < qlim;
+  const int rqc = qvalid ? rq : 0;
+  const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  const int32_t qoff = row_offset(g, grp, xq);
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + qoff + s * 16 + half * 8));
+    df[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(dO + qoff + s * 16 + half * 8));
+  }
+  const float lse2 = a.lse[size_t(grp) * g.L + xq] * kLog2e;
+  const float dl = a.delta[size_t(grp) * g.L + xq];
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dqacc[dt][v] = 0.f;
+
+  const int c = tid % CH, kg = tid / CH;
+  u32x4 kreg[KPT], vreg[KPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int p = t * KT + kg * KPT + u;
+      const bool ok = p < nkeys;
+      const int pc = ok ? p : 0;
+      const int32_t x = DENSE ? pc : stream_token(g, cols, uint32_t(pc));
+      const int32_t off = row_offset(g, grp, x) + c * 8;
+      u32x4 kk = *reinterpret_cast<const u32x4*>(K + off);
+      u32x4 vv = *reinterpret_cast<const u32x4*>(V + off);
+      if (!ok) {
+        kk = u32x4{0u, 0u, 0u, 0u};
+        vv = u32x4{0u, 0u, 0u, 0u};
+      }
+      kreg[u] = kk;
+      vreg[u] = vv;
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint16_t* Ks = smem + st * STAGE;
+    uint16_t* Vs = Ks + KT * RSTR;
+    uint16_t* Kt = Vs + KT * RSTR;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      *reinterpret_cast<u32x4*>(Ks + (kg * KPT + u) * RSTR + c * 8) = kreg[u];
+      *reinterpret_cast<u32x4*>(Vs + (kg * KPT + u) * RSTR + c * 8) = vreg[u];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t packed[KPT / 2];
+#pragma unroll
+      for (int u = 0; u < KPT; u += 2) {
+        const uint32_t lo = (kreg[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (kreg[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        packed[u / 2] = lo | (hi << 16);
+      }
+      uint16_t* dst = Kt + (c * 8 + e) * TSTR + kg * KPT;
+      if constexpr (KPT == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = packed[0];
+      } else {
+        static_assert(KPT == 4, "KPT");
+        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      }
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const uint16_t* Ks = smem + st * STAGE;
+    const uint16_t* Vs = Ks + KT * RSTR;
+    const uint16_t* Kt = Vs + KT * RSTR;
+    f32x16 sacc[KSUB], dpacc[KSUB];
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sacc[kk][v] = 0.f;
+        dpacc[kk][v] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const int ro = (kk * 32 + l32) * RSTR + s * 16 + half * 8;
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + ro));
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + ro));
+        sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kk], 0, 0, 0);
+        dpacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[s], dpacc[kk], 0, 0, 0);
+      }
+    }
+    const bool ragged = t * KT + KT > nkeys;
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kk][v], c2, -lse2));
+        if (ragged) {
+          const int key = t * KT + kk * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key >= nkeys) pv = 0.f;
+        }
+        dpacc[kk][v] = pv * (dpacc[kk][v] - dl);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 2 * KSUB; ++ks) {
+      const int kk = ks >> 1, g0 = (ks & 1) * 8;
+      u32x4 sw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sw[e] = pack_bf16x2(dpacc[kk][g0 + 2 * e], dpacc[kk][g0 + 2 * e + 1]);
+      const bf16x8 sb = as_bf16x8(sw);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int ro = (dt * 32 + l32) * TSTR + ks * 16 + half * 4;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(Kt + ro);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(Kt + ro + 8);
+        dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dqacc[dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = dt * 32 + gq * 8 + half * 4;
+        const float sc = a.scale;
+        store4(dQ + qoff + d0, dqacc[dt][4 * gq] * sc, dqacc[dt][4 * gq + 1] * sc,
+               dqacc[dt][4 * gq + 2] * sc, dqacc[dt][4 * gq + 3] * sc);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// fp32 instances (VALU): the same recurrences one query (dQ) or one key (dK, dV) per lane.
+template <int D, bool DENSE>
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(AttnParams a) {
+  constexpr int KT = 32;
+  __shared__ float ks[KT][D];
+  __shared__ float vs[KT][D];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[1];
+  const Geom& g = a.g;
+  const int rows = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int qt = bid % a.tiles;
+  bid /= a.tiles;
+  const int iblk = bid % rows;
+  const int grp = bid / rows;
+  const float* Q = static_cast<const float*>(a.q);
+  const float* K = static_cast<const float*>(a.k);
+  const float* V = static_cast<const float*>(a.v);
+  const float* dO = static_cast<const float*>(a.dout);
+  float* dQ = static_cast<float*>(a.dq);
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    nkeys = compact_list<64>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, cols,
+                             scratch) * g.S;
+  }
+  const int qlim = DENSE ? g.L : g.S;
+  const int rq = qt * 64 + threadIdx.x;
+  const bool qvalid = rq < qlim;
+  const int rqc = qvalid ? rq : 0;
+  const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  const int32_t qoff = row_offset(g, grp, xq);
+  float qv[D], dov[D], acc[D];
+  for (int d = 0; d < D; ++d) {
+    qv[d] = Q[qoff + d];
+    dov[d] = dO[qoff + d];
+    acc[d] = 0.f;
+  }
+  const float lse = a.lse[size_t(grp) * g.L + xq];
+  const float dl = a.delta[size_t(grp) * g.L + xq];
+  for (int t0 = 0; t0 < nkeys; t0 += KT) {
+    for (int idx = threadIdx.x; idx < KT * D; idx += 64) {
+      const int kk = idx / D, d = idx % D;
+      const int p = t0 + kk;
+      float kv = 0.f, vv = 0.f;
+      if (p < nkeys) {
+        const int32_t x = DENSE ? p : stream_token(g, cols, uint32_t(p));
+        const int32_t off = row_offset(g, grp, x) + d;
+        kv = K[off];
+        vv = V[off];
+      }
+      ks[kk][d] = kv;
+      vs[kk][d] = vv;
+    }
+    __syncthreads();
+    const int n = min(KT, nkeys - t0);
+    for (int kk = 0; kk < n; ++kk) {
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(qv[d], ks[kk][d], s);
+        dp = fmaf(dov[d], vs[kk][d], dp);
+      }
+      const float p = expf(s * a.scale - lse);
+      const float ds = p * (dp - dl);
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[kk][d], acc[d]);
+    }
+    __syncthreads();
+  }
+  if (qvalid)
+    for (int d = 0; d < D; ++d) dQ[qoff + d] = acc[d] * a.scale;
+}
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(AttnParams a) {
+  constexpr int QT = 32;
+  __shared__ float qs[QT][D];
+  __shared__ float os[QT][D];
+  __shared__ float ls[QT], dls[QT];
+  __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[1];
+  const Geom& g = a.g;
+  const int nrow = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int kt = bid % a.tiles;
+  bid /= a.tiles;
+  const int jblk = bid % nrow;
+  const int grp = bid / nrow;
+  const float* Q = static_cast<const float*>(a.q);
+  const float* K = static_cast<const float*>(a.k);
+  const float* V = static_cast<const float*>(a.v);
+  const float* dO = static_cast<const float*>(a.dout);
+  float* dK = static_cast<float*>(a.dk);
+  float* dV = static_cast<float*>(a.dv);
+  int nq;
+  if constexpr (DENSE) {
+    nq = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.col_ptr, grp, jblk, &start, &len);
+    nq = compact_list<64>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, rows_l,
+                          scratch) * g.S;
+  }
+  const int klim = DENSE ? g.L : g.S;
+  const int rk = kt * 64 + threadIdx.x;
+  const bool kvalid = rk < klim;
+  const int rkc = kvalid ? rk : 0;
+  const int32_t xk = DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
+  const int32_t koff = row_offset(g, grp, xk);
+  float kv[D], vv[D], dk[D], dv[D];
+  for (int d = 0; d < D; ++d) {
+    kv[d] = K[koff + d];
+    vv[d] = V[koff + d];
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  const float* lse_g = a.lse + size_t(grp) * g.L;
+  const float* dl_g = a.delta + size_t(grp) * g.L;
+  for (int t0 = 0; t0 < nq; t0 += QT) {
+    for (int idx = threadIdx.x; idx < QT * D; idx += 64) {
+      const int qq = idx / D, d = idx % D;
+      const int p = t0 + qq;
+      float qval = 0.f, oval = 0.f;
+      if (p < nq) {
+        const int32_t x = DENSE ? p : stream_token(g, rows_l, uint32_t(p));
+        const int32_t off = row_offset(g, grp, x) + d;
+        qval = Q[off];
+        oval = dO[off];
+        if (d == 0) {
+          ls[qq] = lse_g[x];
+          dls[qq] = dl_g[x];
+        }
+      }
+      qs[qq][d] = qval;
+      os[qq][d] = oval;
+    }
+    __syncthreads();
+    const int n = min(QT, nq - t0);
+    for (int qq = 0; qq < n; ++qq) {
+      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(qs[qq][d], kv[d], s);
+        dp = fmaf(os[qq][d], vv[d], dp);
+      }
+      const float p = expf(s * a.scale - ls[qq]);
+      const float ds = p * (dp - dls[qq]);
+      for (int d = 0; d < D; ++d) {
+        dv[d] = fmaf(p, os[qq][d], dv[d]);
+        dk[d] = fmaf(ds, qs[qq][d], dk[d]);
+      }
+    }
+    __syncthreads();
+  }
+  if (kvalid)
+    for (int d = 0; d < D; ++d) {
+      dK[koff + d] = dk[d] * a.scale;
+      dV[koff + d] = dv[d];
+    }
+}
+
+// ---------------------------------------------------------------------------------
+template <typename T, int D>
+static void launch_delta(const Geom& g, const void* o, const void* dout, float* delta,
+                         hipStream_t s) {
+  constexpr int LPR = D / (16 / sizeof(T));
+  const size_t rows = size_t(g.B) * g.L * g.Hh;
+  const int grid = int((rows * LPR + 255) / 256);
+  delta_kernel<T, D><<<grid, 256, 0, s>>>(g, static_cast<const T*>(o),
+                                         static_cast<const T*>(dout), delta);
+}
+
+template <int D, bool DENSE, typename GT>
+static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  // staging splits need an even number of rows per thread: 4 waves at d = 128, 2 at 64
+  constexpr int NWK = D == 128 ? 4 : 2;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
+  attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, GT><<<g.B * g.Hh * rows * a.tiles, NWK * 64, 0, s>>>(a);
+}
+
+template <int D, bool DENSE, typename GT>
+static void launch_dq_bf16(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  constexpr int KSUB = D == 128 ? 1 : 2;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + 127) / 128;
+  attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, GT><<<g.B * g.Hh * rows * a.tiles, 256, 0, s>>>(a);
+}
+
+template <int D, bool DENSE>
+static void launch_dkdv_f32(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + 63) / 64;
+  attn_bwd_dkdv_f32_kernel<D, DENSE><<<g.B * g.Hh * rows * a.tiles, 64, 0, s>>>(a);
+}
+
+template <int D, bool DENSE>
+static void launch_dq_f32(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + 63) / 64;
+  attn_bwd_dq_f32_kernel<D, DENSE><<<g.B * g.Hh * rows * a.tiles, 64, 0, s>>>(a);
+}
+
+// Instantiate launcher L<D, DENSE, GT> for the problem's head_dim, mode and grad type.
+#define VMOBA_DISPATCH_BF16(L, a, s, dense)                                      \
+  do {                                                                          \
+    const bool g32_ = (a).g.grad_dtype == VMOBA_FP32;                           \
+    if ((a).g.D == 128) {                                                       \
+      if (dense) { if (g32_) L<128, true, float>(a, s); else L<128, true, uint16_t>(a, s); } \
+      else { if (g32_) L<128, false, float>(a, s); else L<128, false, uint16_t>(a, s); }    \
+    } else {                                                                    \
+      if (dense) { if (g32_) L<64, true, float>(a, s); else L<64, true, uint16_t>(a, s); }   \
+      else { if (g32_) L<64, false, float>(a, s); else L<64, false, uint16_t>(a, s); }      \
+    }                                                                           \
+  } while (0)
+
+#define VMOBA_DISPATCH_F32(L, a, s, dense)                                       \
+  do {                                                                          \
+    if ((a).g.D == 128) { if (dense) L<128, true>(a, s); else L<128, false>(a, s); } \
+    else { if (dense) L<64, true>(a, s); else L<64, false>(a, s); }             \
+  } while (0)
+
+static AttnParams bwd_params(const Geom& g, const void* q, const void* k, const void* v,
+                             const float* lse, const float* delta, const void* dout) {
+  AttnParams a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = const_cast<float*>(lse);
+  a.delta = const_cast<float*>(delta);
+  a.scale = 1.0f / sqrtf(float(g.D));
+  a.scale_log2 = kLog2e * a.scale;
+  return a;
+}
+
+int launch_bwd_delta(const Geom& g, const void* o, const void* dout, float* delta,
+                     void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.dtype == VMOBA_BF16) {
+    if (g.D == 128) launch_delta<uint16_t, 128>(g, o, dout, delta, s);
+    else launch_delta<uint16_t, 64>(g, o, dout, delta, s);
+  } else {
+    if (g.D == 128) launch_delta<float, 128>(g, o, dout, delta, s);
+    else launch_delta<float, 64>(g, o, dout, delta, s);
+  }
+  return launch_status();
+}
+
+int launch_bwd_dkdv(const Geom& g, bool dense, const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dout,
+                    const int32_t* col_ptr, const int32_t* row_idx, void* dk, void* dv,
+                    void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a = bwd_params(g, q, k, v, lse, delta, dout);
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.dk = dk;
+  a.dv = dv;
+  if (g.dtype == VMOBA_BF16) VMOBA_DISPATCH_BF16(launch_dkdv_bf16, a, s, dense);
+  else VMOBA_DISPATCH_F32(launch_dkdv_f32, a, s, dense);
+  return launch_status();
+}
+
+int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const void* v,
+                  const float* lse, const float* delta, const void* dout,
+                  const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a = bwd_params(g, q, k, v, lse, delta, dout);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.dq = dq;
+  if (g.dtype == VMOBA_BF16) VMOBA_DISPATCH_BF16(launch_dq_bf16, a, s, dense);
+  else VMOBA_DISPATCH_F32(launch_dq_f32, a, s, dense);
+  return launch_status();
+}
+
+}  // namespace vmoba

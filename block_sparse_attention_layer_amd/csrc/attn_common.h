@@ -1,0 +1,92 @@
+// Shared pieces of the attention kernels: parameters, head-group decoding, the
+// gathered token stream of a block list, and list compaction into LDS.
+//
+// A query block i attends to the concatenated tokens of the key blocks in its list
+// (papernotes 方法详解/整体框架: attention only on the selected blocks).  That concatenation
+// is walked as one "token stream": position p is token p % S of the (p / S)-th listed
+// block, so tiles of the stream cross block boundaries and only the stream's last tile
+// is ragged.  The same stream, built from a column list, gives the query tokens that
+// attend to one key block in the backward pass.
+#pragma once
+
+#include "device_common.h"
+
+namespace vmoba {
+
+struct AttnParams {
+  Geom g;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;       // forward output (read by the backward)
+  const void* dout;
+  void* out;           // forward: O; unused in backward
+  float* lse;          // [G][L]
+  float* delta;        // [G][L] (backward)
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* col_ptr;
+  const int32_t* row_idx;
+  int32_t tiles;       // tiles per block row (query tiles fwd/dq, key tiles dkdv)
+  float scale;         // 1/sqrt(d)
+  float scale_log2;    // log2(e)/sqrt(d)
+};
+
+// Element offset of token x of head group grp in a [B][L][Hh][D] tensor.
+__device__ __forceinline__ int32_t row_offset(const Geom& g, int grp, int32_t x) {
+  const int b = grp / g.Hh, h = grp - b * g.Hh;
+  return ((b * g.L + x) * g.Hh + h) * g.D;
+}
+
+// Token of stream position p over the block list `lst` (already validated).
+__device__ __forceinline__ int32_t stream_token(const Geom& g, const int32_t* lst,
+                                                uint32_t p) {
+  const uint32_t bi = fd_div(p, g.div_S);
+  const uint32_t r = p - bi * uint32_t(g.S);
+  return block_base(g, uint32_t(lst[bi])) + block_offset(g, r);
+}
+
+// Copy the entries of list[0, n) that lie in [0, Nb) into lds[], keeping their order;
+// returns how many were kept.  All threads of the workgroup must call it.  `scratch`
+// needs one int per wave.
+template <int NT>
+__device__ int compact_list(const int32_t* __restrict__ list, int n, int Nb, int32_t* lds,
+                            int32_t* scratch) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int kept = 0;
+  for (int base = 0; base < n; base += NT) {
+    const int t = base + threadIdx.x;
+    const int32_t j = t < n ? list[t] : -1;
+    const bool ok = j >= 0 && j < Nb;
+    const unsigned long long m = __ballot(ok);
+    if (lane == 0) scratch[w] = __popcll(m);
+    __syncthreads();
+    int off = kept, tot = 0;
+    for (int i = 0; i < NWV; ++i) {
+      if (i < w) off += scratch[i];
+      tot += scratch[i];
+    }
+    if (ok) lds[off + __popcll(m & ((1ull << lane) - 1ull))] = j;
+    kept += tot;
+    __syncthreads();
+  }
+  return kept;
+}
+
+// Validated [start, start + len) range of list `which` of head group grp.
+__device__ __forceinline__ void list_range(const Geom& g, const int32_t* ptr, int grp,
+                                           int row, int* start, int* len) {
+  const int cap = g.Nb * g.Nb;
+  const int32_t* rp = ptr + grp * (g.Nb + 1);
+  int s = rp[row], e = rp[row + 1];
+  s = min(max(s, 0), cap);
+  e = min(max(e, s), min(cap, s + g.Nb));
+  *start = s;
+  *len = e - s;
+}
+
+}  // namespace vmoba

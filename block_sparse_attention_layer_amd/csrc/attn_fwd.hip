@@ -1,0 +1,378 @@
+// Block-sparse (and dense) flash attention forward for gfx950.
+//
+// papernotes 方法详解/整体框架 and paperlayer §3.1: each query block attends only to the
+// tokens of its selected key blocks; the output keeps full attention's shape.
+//
+// bf16 kernel, per workgroup: NW waves x 32 queries of one query block, all sharing the
+// block's key stream.  Per key tile (KT = 32*KSUB keys) the workgroup stages K row-major
+// and V transposed in LDS (double-buffered, padded rows, global loads of tile t+1 in
+// flight while tile t is computed).  Each wave computes S^T = K Q^T on
+// v_mfma_f32_32x32x16_bf16 with its Q fragments held in registers, so every lane owns
+// one query column: the online-softmax max needs one exchange between the two lane
+// halves, the row sum none until the end, and rescaling O is a per-lane multiply.
+// P^T stays in registers as the B operand of O^T += V^T P^T; the k-order of that product
+// is permuted to match the S^T accumulator layout, and the V^T reads follow the same
+// permutation.  exp2 with the log2(e)/sqrt(d) scale folded into one FMA; fp32
+// accumulation throughout; O rescaled by 1/l and written back in natural token order
+// with LSE = m/sqrt(d) + ln l.
+#include <math.h>
+
+#include "attn_common.h"
+
+namespace vmoba {
+
+template <int D, int NW, int KSUB, bool DENSE>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
+  constexpr int NT = NW * 64;
+  constexpr int QT = NW * 32;
+  constexpr int KT = KSUB * 32;
+  constexpr int CH = D / 8;                 // 16-byte chunks per row
+  constexpr int KPT = KT * CH / NT;         // keys staged per thread
+  static_assert(KT * CH % NT == 0 && NT % CH == 0, "staging split");
+  static_assert(KPT % 2 == 0, "V^T staging packs key pairs");
+  constexpr int KSTR = D + 8;               // K row stride (bf16)
+  constexpr int VSTR = KT + 4;              // V^T row stride (bf16)
+  constexpr int STAGE = KT * KSTR + D * VSTR;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[NW];
+
+  const Geom& g = a.g;
+  const int rows = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int qt = bid % a.tiles;
+  bid /= a.tiles;
+  const int iblk = bid % rows;
+  const int grp = bid / rows;
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  uint16_t* __restrict__ O = static_cast<uint16_t*>(a.out);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  // key stream
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, cols, scratch);
+    nkeys = kept * g.S;
+  }
+  const int ntiles = (nkeys + KT - 1) / KT;
+
+  // this lane's query
+  const int qlim = DENSE ? g.L : g.S;
+  const int rq = qt * QT + w * 32 + l32;
+  const bool qvalid = rq < qlim;
+  const int rqc = qvalid ? rq : 0;
+  const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  const int32_t qoff = row_offset(g, grp, xq);
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + qoff + s * 16 + half * 8));
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  // staging role
+  const int c = tid % CH, kg = tid / CH;
+  u32x4 kreg[KPT], vreg[KPT];
+
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int p = t * KT + kg * KPT + u;
+      const bool ok = p < nkeys;
+      const int pc = ok ? p : 0;
+      const int32_t x = DENSE ? pc : stream_token(g, cols, uint32_t(pc));
+      const int32_t off = row_offset(g, grp, x) + c * 8;
+      u32x4 kk = *reinterpret_cast<const u32x4*>(K + off);
+      u32x4 vv = *reinterpret_cast<const u32x4*>(V + off);
+      if (!ok) {
+        kk = u32x4{0u, 0u, 0u, 0u};
+        vv = u32x4{0u, 0u, 0u, 0u};
+      }
+      kreg[u] = kk;
+      vreg[u] = vv;
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint16_t* Ks = smem + st * STAGE;
+    uint16_t* Vt = Ks + KT * KSTR;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      *reinterpret_cast<u32x4*>(Ks + (kg * KPT + u) * KSTR + c * 8) = kreg[u];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t packed[KPT / 2];
+#pragma unroll
+      for (int u = 0; u < KPT; u += 2) {
+        const uint32_t lo = (vreg[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const uint32_t hi = (vreg[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        packed[u / 2] = lo | (hi << 16);
+      }
+      uint16_t* dst = Vt + (c * 8 + e) * VSTR + kg * KPT;
+      if constexpr (KPT == 2) {
+        *reinterpret_cast<uint32_t*>(dst) = packed[0];
+      } else if constexpr (KPT == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT / 2; u += 4)
+          *reinterpret_cast<u32x4*>(dst + 2 * u) =
+              u32x4{packed[u], packed[u + 1], packed[u + 2], packed[u + 3]};
+      }
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const uint16_t* Ks = smem + st * STAGE;
+    const uint16_t* Vt = Ks + KT * KSTR;
+
+    // S^T tile: keys along MFMA rows, this lane's query along the column
+    f32x16 sacc[KSUB];
+#pragma unroll
+    for (int kt = 0; kt < KSUB; ++kt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 ka = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(Ks + (kt * 32 + l32) * KSTR + s * 16 + half * 8));
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    // mask the ragged end of the stream
+    if (t * KT + KT > nkeys) {
+#pragma unroll
+      for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = t * KT + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key >= nkeys) sacc[kt][v] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    const float moff = m_new * c2;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], c2, -moff));
+        sacc[kt][v] = pv;
+        psum += pv;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int ks = 0; ks < 2 * KSUB; ++ks) {
+      const int kt = ks >> 1, g0 = (ks & 1) * 8;
+      u32x4 pw;
+      pw[0] = pack_bf16x2(sacc[kt][g0 + 0], sacc[kt][g0 + 1]);
+      pw[1] = pack_bf16x2(sacc[kt][g0 + 2], sacc[kt][g0 + 3]);
+      pw[2] = pack_bf16x2(sacc[kt][g0 + 4], sacc[kt][g0 + 5]);
+      pw[3] = pack_bf16x2(sacc[kt][g0 + 6], sacc[kt][g0 + 7]);
+      const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* vp = Vt + (dt * 32 + l32) * VSTR + ks * 16 + half * 4;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(st ^ 1);
+    __syncthreads();
+  }
+
+  // finalise
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const bool empty = nkeys == 0;
+  const float inv = empty ? 0.f : 1.0f / l_tot;
+  if (qvalid) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = dt * 32 + gq * 8 + half * 4;
+        u32x2 out;
+        out[0] = pack_bf16x2(oacc[dt][4 * gq + 0] * inv, oacc[dt][4 * gq + 1] * inv);
+        out[1] = pack_bf16x2(oacc[dt][4 * gq + 2] * inv, oacc[dt][4 * gq + 3] * inv);
+        *reinterpret_cast<u32x2*>(O + qoff + d0) = out;
+      }
+    if (half == 0)
+      a.lse[size_t(grp) * g.L + xq] = empty ? -INFINITY : m_run * a.scale + logf(l_tot);
+  }
+}
+
+// fp32 instance (VALU, one query per lane): the plain online-softmax recurrence over the
+// same key stream, for fp32 inputs.
+template <int D, bool DENSE>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams a) {
+  constexpr int KT = 32;
+  __shared__ float ks[KT][D];
+  __shared__ float vs[KT][D];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t scratch[1];
+  const Geom& g = a.g;
+  const int rows = DENSE ? 1 : g.Nb;
+  int bid = blockIdx.x;
+  const int qt = bid % a.tiles;
+  bid /= a.tiles;
+  const int iblk = bid % rows;
+  const int grp = bid / rows;
+  const float* Q = static_cast<const float*>(a.q);
+  const float* K = static_cast<const float*>(a.k);
+  const float* V = static_cast<const float*>(a.v);
+  float* O = static_cast<float*>(a.out);
+
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    nkeys = compact_list<64>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, cols,
+                             scratch) * g.S;
+  }
+  const int qlim = DENSE ? g.L : g.S;
+  const int rq = qt * 64 + threadIdx.x;
+  const bool qvalid = rq < qlim;
+  const int rqc = qvalid ? rq : 0;
+  const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  const int32_t qoff = row_offset(g, grp, xq);
+  float qv[D], acc[D];
+  for (int d = 0; d < D; ++d) {
+    qv[d] = Q[qoff + d] * a.scale;
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int t0 = 0; t0 < nkeys; t0 += KT) {
+    for (int idx = threadIdx.x; idx < KT * D; idx += 64) {
+      const int kk = idx / D, d = idx % D;
+      const int p = t0 + kk;
+      float kv = 0.f, vv = 0.f;
+      if (p < nkeys) {
+        const int32_t x = DENSE ? p : stream_token(g, cols, uint32_t(p));
+        const int32_t off = row_offset(g, grp, x) + d;
+        kv = K[off];
+        vv = V[off];
+      }
+      ks[kk][d] = kv;
+      vs[kk][d] = vv;
+    }
+    __syncthreads();
+    const int n = min(KT, nkeys - t0);
+    for (int kk = 0; kk < n; ++kk) {
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(qv[d], ks[kk][d], s);
+      const float mn = fmaxf(m, s);
+      const float al = expf(m - mn);
+      const float p = expf(s - mn);
+      l = l * al + p;
+      for (int d = 0; d < D; ++d) acc[d] = acc[d] * al + p * vs[kk][d];
+      m = mn;
+    }
+    __syncthreads();
+  }
+  if (qvalid) {
+    const float inv = nkeys ? 1.0f / l : 0.f;
+    for (int d = 0; d < D; ++d) O[qoff + d] = acc[d] * inv;
+    a.lse[size_t(grp) * g.L + xq] = nkeys ? m + logf(l) : -INFINITY;
+  }
+}
+
+template <int D, int NW, int KSUB, bool DENSE>
+static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int qlim = DENSE ? g.L : g.S;
+  a.tiles = (qlim + NW * 32 - 1) / (NW * 32);
+  const int rows = DENSE ? 1 : g.Nb;
+  const int grid = g.B * g.Hh * rows * a.tiles;
+  attn_fwd_bf16_kernel<D, NW, KSUB, DENSE><<<grid, NW * 64, 0, s>>>(a);
+}
+
+template <int D, bool DENSE>
+static void launch_fwd_f32(AttnParams& a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int qlim = DENSE ? g.L : g.S;
+  a.tiles = (qlim + 63) / 64;
+  const int rows = DENSE ? 1 : g.Nb;
+  attn_fwd_f32_kernel<D, DENSE><<<g.B * g.Hh * rows * a.tiles, 64, 0, s>>>(a);
+}
+
+int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
+                    const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                    void* o, float* lse, void* ws, void* stream) {
+  (void)ws;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = o;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.scale = 1.0f / sqrtf(float(g.D));
+  a.scale_log2 = kLog2e * a.scale;
+  if (g.dtype == VMOBA_BF16) {
+    if (g.D == 128) {
+      if (dense) launch_fwd_bf16<128, 4, 2, true>(a, s);
+      else launch_fwd_bf16<128, 4, 2, false>(a, s);
+    } else {
+      if (dense) launch_fwd_bf16<64, 4, 2, true>(a, s);
+      else launch_fwd_bf16<64, 4, 2, false>(a, s);
+    }
+  } else {
+    if (g.D == 128) {
+      if (dense) launch_fwd_f32<128, true>(a, s);
+      else launch_fwd_f32<128, false>(a, s);
+    } else {
+      if (dense) launch_fwd_f32<64, true>(a, s);
+      else launch_fwd_f32<64, false>(a, s);
+    }
+  }
+  return launch_status();
+}
+
+}  // namespace vmoba

@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (api.cpp, validate.cpp) and the kernel
+// launchers (*.hip).  Host code only; no HIP types so that it builds with g++.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/vmoba.h"
+#include "geometry.h"
+
+namespace vmoba {
+
+// Largest block count the selection and sparse attention calls accept: the selection
+// kernel keeps the N_b x N_b pair bitmap of one head in LDS (128 KiB at 1024 blocks).
+constexpr int kMaxBlocks = 1024;
+
+int validate_problem(const vmoba_problem* p);
+Geom make_geom(const vmoba_problem* p);
+int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes);
+
+// Launchers: enqueue on `stream` (a hipStream_t) and return VMOBA_OK or VMOBA_ERR_HIP.
+int launch_pool(const Geom& g, const void* q, const void* k, float* q_pool,
+                float* k_pool, void* stream);
+
+int launch_select(const Geom& g, const float* q_pool, const float* k_pool, float tau,
+                  int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
+                  int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
+                  void* stream);
+
+int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
+                    const void* v, const int32_t* row_ptr, const int32_t* col_idx,
+                    void* o, float* lse, void* ws, void* stream);
+
+int launch_bwd_delta(const Geom& g, const void* o, const void* dout, float* delta,
+                     void* stream);
+
+int launch_bwd_dkdv(const Geom& g, bool dense, const void* q, const void* k, const void* v,
+                    const float* lse, const float* delta, const void* dout,
+                    const int32_t* col_ptr, const int32_t* row_idx, void* dk, void* dv,
+                    void* stream);
+
+int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const void* v,
+                  const float* lse, const float* delta, const void* dout,
+                  const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* stream);
+
+}  // namespace vmoba

@@ -1,0 +1,137 @@
+// Host-only part of the C ABI: argument validation, geometry, workspace sizes and
+// status strings.  Built without HIP so that it can also be linked into host tests.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/vmoba.h"
+#include "geometry.h"
+#include "internal.h"
+
+namespace vmoba {
+
+int validate_problem(const vmoba_problem* p) {
+  if (!p) return VMOBA_ERR_NULL;
+  if (p->batch <= 0 || p->heads <= 0 || p->T <= 0 || p->H <= 0 || p->W <= 0 ||
+      p->bt <= 0 || p->bh <= 0 || p->bw <= 0 || p->layer_idx < 0)
+    return VMOBA_ERR_SHAPE;
+  if (p->T % p->bt || p->H % p->bh || p->W % p->bw) return VMOBA_ERR_SHAPE;
+  if (p->dtype != VMOBA_BF16 && p->dtype != VMOBA_FP32) return VMOBA_ERR_DTYPE;
+  if (p->grad_dtype != VMOBA_BF16 && p->grad_dtype != VMOBA_FP32) return VMOBA_ERR_DTYPE;
+  if (p->dtype == VMOBA_FP32 && p->grad_dtype != VMOBA_FP32) return VMOBA_ERR_DTYPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return VMOBA_ERR_HEAD_DIM;
+  const int mode = p->layer_idx % 3;
+  if (mode == 0 && (p->bh != p->H || p->bw != p->W)) return VMOBA_ERR_MODE;
+  if (mode == 1 && p->bt != p->T) return VMOBA_ERR_MODE;
+  // Every element count and index used on the device stays below 2^31.
+  const int64_t L = int64_t(p->T) * p->H * p->W;
+  const int64_t elems = int64_t(p->batch) * L * p->heads * p->head_dim;
+  const int64_t nb = (int64_t(p->T) / p->bt) * (p->H / p->bh) * (p->W / p->bw);
+  const int64_t groups = int64_t(p->batch) * p->heads;
+  if (L >= (int64_t(1) << 31) || elems >= (int64_t(1) << 31) ||
+      groups * L >= (int64_t(1) << 31) || groups * nb * nb >= (int64_t(1) << 31) ||
+      nb * nb >= (int64_t(1) << 31))
+    return VMOBA_ERR_OVERFLOW;
+  return VMOBA_OK;
+}
+
+Geom make_geom(const vmoba_problem* p) {
+  Geom g;
+  g.B = p->batch;
+  g.Hh = p->heads;
+  g.D = p->head_dim;
+  g.T = p->T;
+  g.H = p->H;
+  g.W = p->W;
+  g.L = p->T * p->H * p->W;
+  g.bt = p->bt;
+  g.bh = p->bh;
+  g.bw = p->bw;
+  g.nt = p->T / p->bt;
+  g.nh = p->H / p->bh;
+  g.nw = p->W / p->bw;
+  g.Nb = g.nt * g.nh * g.nw;
+  g.S = p->bt * p->bh * p->bw;
+  g.mode = p->layer_idx % 3;
+  g.dtype = p->dtype;
+  g.grad_dtype = p->grad_dtype;
+  g.div_S = make_fastdiv(uint32_t(g.S));
+  g.div_nhnw = make_fastdiv(uint32_t(g.nh * g.nw));
+  g.div_nw = make_fastdiv(uint32_t(g.nw));
+  g.div_bhbw = make_fastdiv(uint32_t(g.bh * g.bw));
+  g.div_bw = make_fastdiv(uint32_t(g.bw));
+  return g;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
+  const Geom g = make_geom(p);
+  const size_t groups = size_t(g.B) * g.Hh;
+  const size_t pool = size_t(g.Nb) * g.Nb;
+  switch (op) {
+    case VMOBA_OP_POOL:
+    case VMOBA_OP_DENSE_FWD:
+      *bytes = 0;
+      return VMOBA_OK;
+    case VMOBA_OP_SELECT:
+      // raw block scores, fp32 per head group
+      *bytes = align256(groups * pool * sizeof(float));
+      return VMOBA_OK;
+    case VMOBA_OP_SPARSE_FWD:
+      // per-head-group row order, longest rows first (launch scheduling)
+      *bytes = align256(groups * g.Nb * sizeof(int32_t));
+      return VMOBA_OK;
+    case VMOBA_OP_SPARSE_BWD:
+      // delta = rowsum(dO * O) fp32 [B][Hh][L] + row and column orders
+      *bytes = align256(groups * size_t(g.L) * sizeof(float)) +
+               2 * align256(groups * g.Nb * sizeof(int32_t));
+      return VMOBA_OK;
+    case VMOBA_OP_DENSE_BWD:
+      *bytes = align256(groups * size_t(g.L) * sizeof(float));
+      return VMOBA_OK;
+    default:
+      return VMOBA_ERR_OP;
+  }
+}
+
+}  // namespace vmoba
+
+extern "C" {
+
+const char* vmoba_version(void) { return "vmoba-gfx950 0.1.0"; }
+
+const char* vmoba_status_string(int status) {
+  switch (status) {
+    case VMOBA_OK: return "ok";
+    case VMOBA_ERR_NULL: return "null pointer argument";
+    case VMOBA_ERR_SHAPE: return "bad shape: sizes must be positive and the block shape must divide (T, H, W)";
+    case VMOBA_ERR_MODE: return "block shape does not match the partition mode layer_idx % 3";
+    case VMOBA_ERR_TAU: return "tau must be finite and in (0, 1]";
+    case VMOBA_ERR_DTYPE: return "unsupported dtype";
+    case VMOBA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case VMOBA_ERR_WORKSPACE: return "workspace too small";
+    case VMOBA_ERR_OVERFLOW: return "problem too large for 32-bit indexing";
+    case VMOBA_ERR_HIP: return "HIP runtime error";
+    case VMOBA_ERR_OP: return "unknown op";
+    default: return "unknown status";
+  }
+}
+
+int vmoba_validate(const vmoba_problem* p) { return vmoba::validate_problem(p); }
+
+int vmoba_num_blocks(const vmoba_problem* p, int32_t* nb) {
+  int st = vmoba::validate_problem(p);
+  if (st) return st;
+  if (!nb) return VMOBA_ERR_NULL;
+  *nb = vmoba::make_geom(p).Nb;
+  return VMOBA_OK;
+}
+
+int vmoba_workspace_size(const vmoba_problem* p, int op, size_t* bytes) {
+  int st = vmoba::validate_problem(p);
+  if (st) return st;
+  if (!bytes) return VMOBA_ERR_NULL;
+  return vmoba::workspace_bytes(p, op, bytes);
+}
+
+}  // extern "C"
