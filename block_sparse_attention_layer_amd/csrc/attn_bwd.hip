@@ -68,19 +68,21 @@ __device__ __forceinline__ void store4(GT* dst, float a, float b, float c, float
 // ---------------------------------------------------------------------------------
 // dK, dV: one wave per 32 keys, query stream from the column list of the key block.
 template <int D, int NW, bool DENSE, typename GT>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
-  constexpr int QT = 32;                    // queries per tile
-  constexpr int CH = D / 8;
-  constexpr int QPT = QT * CH / NT;         // queries staged per thread
-  static_assert(QT * CH % NT == 0 && NT % CH == 0 && QPT % 2 == 0, "staging split");
-  constexpr int RSTR = D + 8;               // row-major stride
-  constexpr int TSTR = QT + 4;              // transposed stride
-  constexpr int STAGE = 2 * QT * RSTR + 2 * D * TSTR;
+  constexpr int QT = 32;                     // queries per tile
+  constexpr int ROWB = D * 2;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int LPW = QT / (NW * RPI);
+  static_assert(QT % (NW * RPI) == 0, "tile rows split over waves");
+  constexpr int TILE = QT * ROWB;
+  // per stage: Q tile, dO tile, then 2 x QT floats (lse * log2 e, delta)
+  constexpr int STAGE = 2 * TILE + 2 * QT * 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][QT];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][STAGE];
+  // V rows of this workgroup's keys (B operands of dP = dO V^T), loaded once
+  __shared__ __attribute__((aligned(1024))) unsigned char vtile[NW * 32 * ROWB];
   __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t scratch[NW];
 
@@ -109,23 +111,39 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams 
   } else {
     int start, len;
     list_range(g, a.col_ptr, grp, jblk, &start, &len);
-    nq = compact_list<NT>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, rows_l,
-                          scratch) * g.S;
+    const int kept = compact_list<NT>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, rows_l, scratch);
+    for (int i = tid; i < kept; i += NT) rows_l[i] = block_base(g, uint32_t(rows_l[i]));
+    __syncthreads();
+    nq = kept * g.S;
   }
   const int ntiles = (nq + QT - 1) / QT;
 
+  // this lane's key: K and V fragments as B operands (lane = key, 8 d per k-step)
   const int klim = DENSE ? g.L : g.S;
   const int rk = kt * NW * 32 + w * 32 + l32;
   const bool kvalid = rk < klim;
   const int rkc = kvalid ? rk : 0;
   const int32_t xk = DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
   const int32_t koff = row_offset(g, grp, xk);
-  bf16x8 kf[D / 16], vf[D / 16];
+  bf16x8 kf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
+  for (int s = 0; s < D / 16; ++s)
     kf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + koff + s * 16 + half * 8));
-    vf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(V + koff + s * 16 + half * 8));
+  {
+    // this wave's 32 V rows into vtile (row = wave*32 + key lane), swizzled like a tile
+    constexpr int CPR0 = D / 8;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = w * 32 + i * RPI + lane / CPR0;
+      const int rr = kt * NW * 32 + r;
+      const int rrc = rr < klim ? rr : 0;
+      const int32_t x = DENSE ? rrc : block_base(g, jblk) + block_offset(g, rrc);
+      const int32_t off = row_offset(g, grp, x) + ((lane % CPR0) ^ swz<D>(r)) * 8;
+      load_to_lds16(V + off, vtile + (w * 32 + i * RPI) * ROWB);
+    }
   }
+  const unsigned char* vrow = vtile;
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -135,91 +153,51 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams 
       dvacc[dt][v] = 0.f;
     }
 
-  const int c = tid % CH, qg = tid / CH;
-  u32x4 qreg[QPT], oreg[QPT];
-  float lse_reg = 0.f, dl_reg = 0.f;
   const float* lse_g = a.lse + size_t(grp) * g.L;
   const float* dl_g = a.delta + size_t(grp) * g.L;
-
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      const int p = t * QT + qg * QPT + u;
-      const bool ok = p < nq;
-      const int pc = ok ? p : 0;
-      const int32_t x = DENSE ? pc : stream_token(g, rows_l, uint32_t(pc));
-      const int32_t off = row_offset(g, grp, x) + c * 8;
-      u32x4 qq = *reinterpret_cast<const u32x4*>(Q + off);
-      u32x4 oo = *reinterpret_cast<const u32x4*>(dO + off);
-      if (!ok) {
-        qq = u32x4{0u, 0u, 0u, 0u};
-        oo = u32x4{0u, 0u, 0u, 0u};
-      }
-      qreg[u] = qq;
-      oreg[u] = oo;
-    }
-    if (tid < QT) {
-      const int p = t * QT + tid;
-      if (p < nq) {
-        const int32_t x = DENSE ? p : stream_token(g, rows_l, uint32_t(p));
-        lse_reg = lse_g[x] * kLog2e;
-        dl_reg = dl_g[x];
-      } else {
-        lse_reg = INFINITY;  // P = 0 for padding queries
-        dl_reg = 0.f;
-      }
+  constexpr int CPR = D / 8;
+  const int lrow0 = w * (QT / NW) + lane / CPR;
+  const int lcp = lane % CPR;
+  auto qtoken = [&](int p) -> int32_t {
+    if constexpr (DENSE) {
+      return p;
+    } else {
+      const uint32_t bi = fd_div(uint32_t(p), g.div_S);
+      return rows_l[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
     }
   };
-  auto transpose_store = [&](uint16_t* dst_base, const u32x4* regs) {
+  auto issue_tile = [&](int t, int st) {
+    unsigned char* qb = smem[st];
+    unsigned char* ob = smem[st] + TILE;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t packed[QPT / 2];
-#pragma unroll
-      for (int u = 0; u < QPT; u += 2) {
-        const uint32_t lo = (regs[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        const uint32_t hi = (regs[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        packed[u / 2] = lo | (hi << 16);
-      }
-      uint16_t* dst = dst_base + (c * 8 + e) * TSTR + qg * QPT;
-      if constexpr (QPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = packed[0];
-      } else {
-        static_assert(QPT == 4, "QPT");
-        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
-      }
+    for (int i = 0; i < LPW; ++i) {
+      const int r = lrow0 + i * RPI;
+      const int p = min(t * QT + r, nq - 1);   // padding rows repeat the last query
+      const int32_t off = row_offset(g, grp, qtoken(p)) + (lcp ^ swz<D>(r)) * 8;
+      const int dst = (w * (QT / NW) + i * RPI) * ROWB;
+      load_to_lds16(Q + off, qb + dst);
+      load_to_lds16(dO + off, ob + dst);
     }
-  };
-  auto store_tile = [&](int st) {
-    uint16_t* Qs = smem + st * STAGE;
-    uint16_t* Os = Qs + QT * RSTR;
-    uint16_t* Qt = Os + QT * RSTR;
-    uint16_t* Ot = Qt + D * TSTR;
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-      *reinterpret_cast<u32x4*>(Qs + (qg * QPT + u) * RSTR + c * 8) = qreg[u];
-      *reinterpret_cast<u32x4*>(Os + (qg * QPT + u) * RSTR + c * 8) = oreg[u];
-    }
-    transpose_store(Qt, qreg);
-    transpose_store(Ot, oreg);
-    if (tid < QT) {
-      lse_s[st][tid] = lse_reg;
-      dl_s[st][tid] = dl_reg;
+    if (w == 0) {   // lanes 0-31: lse of the tile's queries; lanes 32-63: delta
+      const int p = min(t * QT + l32, nq - 1);
+      const int32_t x = qtoken(p);
+      const float* src = half ? dl_g + x : lse_g + x;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(smem[st] + 2 * TILE), 4, 0, 0);
     }
   };
 
   const float c2 = a.scale_log2;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_lds_loads();
   __syncthreads();
+  const int grp16 = lane >> 4, sl = lane & 15;
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const uint16_t* Qs = smem + st * STAGE;
-    const uint16_t* Os = Qs + QT * RSTR;
-    const uint16_t* Qt = Os + QT * RSTR;
-    const uint16_t* Ot = Qt + D * TSTR;
+    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
+    const unsigned char* qb = smem[st];
+    const unsigned char* ob = smem[st] + TILE;
+    const float* lse_s = reinterpret_cast<const float*>(smem[st] + 2 * TILE);
+    const float* dl_s = lse_s + QT;
 
     f32x16 sacc, dpacc;
 #pragma unroll
@@ -229,24 +207,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams 
     }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      const bf16x8 qa =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(Qs + l32 * RSTR + s * 16 + half * 8));
-      const bf16x8 oa =
-          as_bf16x8(*reinterpret_cast<const u32x4*>(Os + l32 * RSTR + s * 16 + half * 8));
+      const int o = tile_off<D>(l32, 2 * s + half);
+      const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + o));
+      const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(ob + o));
+      const bf16x8 vb16 = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          vrow + tile_off<D>(w * 32 + l32, 2 * s + half)));
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sacc, 0, 0, 0);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[s], dpacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb16, dpacc, 0, 0, 0);
     }
-    // sacc[v]: query 8*(v/4) + 4*half + v%4 of the tile, key = this lane
+    // sacc[v]: query 8*(v/4) + 4*half + v%4 of the tile; key = this lane
+    const bool ragged = t * QT + QT > nq;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[st][gq * 8 + half * 4]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dl_s[st][gq * 8 + half * 4]);
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + gq * 8 + half * 4);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_s + gq * 8 + half * 4);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
       const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = 4 * gq + r;
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[r]));
+        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[r] * kLog2e));
+        if (ragged && t * QT + 8 * gq + 4 * half + r >= nq) pv = 0.f;
         sacc[v] = pv;
         dpacc[v] = pv * (dpacc[v] - dv4[r]);
       }
@@ -261,20 +242,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams 
         sw[e] = pack_bf16x2(dpacc[g0 + 2 * e], dpacc[g0 + 2 * e + 1]);
       }
       const bf16x8 pb = as_bf16x8(pw), sb = as_bf16x8(sw);
+      const int q0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int ro = (dt * 32 + l32) * TSTR + ks * 16 + half * 4;
-        const u32x2 olo = *reinterpret_cast<const u32x2*>(Ot + ro);
-        const u32x2 ohi = *reinterpret_cast<const u32x2*>(Ot + ro + 8);
-        const u32x2 qlo = *reinterpret_cast<const u32x2*>(Qt + ro);
-        const u32x2 qhi = *reinterpret_cast<const u32x2*>(Qt + ro + 8);
+        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
+        const int bo = (sl & 1) * 8;
+        const int o0 = tile_off<D>(q0, c) + bo, o1 = tile_off<D>(q0 + 8, c) + bo;
+        const u32x2 olo = lds_read_tr16(ob + o0), ohi = lds_read_tr16(ob + o1);
+        const u32x2 qlo = lds_read_tr16(qb + o0), qhi = lds_read_tr16(qb + o1);
         dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]}), pb, dvacc[dt], 0, 0, 0);
         dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dkacc[dt], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile(st ^ 1);
+    wait_lds_loads();
     __syncthreads();
   }
 
@@ -296,18 +278,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_bf16_kernel(AttnParams 
 // ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
 template <int D, int NW, int KSUB, bool DENSE, typename GT>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
   constexpr int QT = NW * 32;
   constexpr int KT = KSUB * 32;
-  constexpr int CH = D / 8;
-  constexpr int KPT = KT * CH / NT;
-  static_assert(KT * CH % NT == 0 && NT % CH == 0 && KPT % 2 == 0, "staging split");
-  constexpr int RSTR = D + 8;
-  constexpr int TSTR = KT + 4;
-  constexpr int STAGE = 2 * KT * RSTR + D * TSTR;
+  constexpr int ROWB = D * 2;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int LPW = KT / (NW * RPI);
+  static_assert(KT % (NW * RPI) == 0, "tile rows split over waves");
+  constexpr int TILE = KT * ROWB;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t scratch[NW];
 
@@ -335,8 +317,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a)
   } else {
     int start, len;
     list_range(g, a.row_ptr, grp, iblk, &start, &len);
-    nkeys = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len, g.Nb, cols,
-                             scratch) * g.S;
+    const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, cols, scratch);
+    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    __syncthreads();
+    nkeys = kept * g.S;
   }
   const int ntiles = (nkeys + KT - 1) / KT;
 
@@ -361,66 +346,40 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dqacc[dt][v] = 0.f;
 
-  const int c = tid % CH, kg = tid / CH;
-  u32x4 kreg[KPT], vreg[KPT];
-  auto load_tile = [&](int t) {
+  constexpr int CPR = D / 8;
+  const int lrow0 = w * (KT / NW) + lane / CPR;
+  const int lcp = lane % CPR;
+  auto issue_tile = [&](int t, int st) {
+    unsigned char* kb = smem[st];
+    unsigned char* vb = smem[st] + TILE;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int p = t * KT + kg * KPT + u;
-      const bool ok = p < nkeys;
-      const int pc = ok ? p : 0;
-      const int32_t x = DENSE ? pc : stream_token(g, cols, uint32_t(pc));
-      const int32_t off = row_offset(g, grp, x) + c * 8;
-      u32x4 kk = *reinterpret_cast<const u32x4*>(K + off);
-      u32x4 vv = *reinterpret_cast<const u32x4*>(V + off);
-      if (!ok) {
-        kk = u32x4{0u, 0u, 0u, 0u};
-        vv = u32x4{0u, 0u, 0u, 0u};
-      }
-      kreg[u] = kk;
-      vreg[u] = vv;
-    }
-  };
-  auto store_tile = [&](int st) {
-    uint16_t* Ks = smem + st * STAGE;
-    uint16_t* Vs = Ks + KT * RSTR;
-    uint16_t* Kt = Vs + KT * RSTR;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      *reinterpret_cast<u32x4*>(Ks + (kg * KPT + u) * RSTR + c * 8) = kreg[u];
-      *reinterpret_cast<u32x4*>(Vs + (kg * KPT + u) * RSTR + c * 8) = vreg[u];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t packed[KPT / 2];
-#pragma unroll
-      for (int u = 0; u < KPT; u += 2) {
-        const uint32_t lo = (kreg[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        const uint32_t hi = (kreg[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        packed[u / 2] = lo | (hi << 16);
-      }
-      uint16_t* dst = Kt + (c * 8 + e) * TSTR + kg * KPT;
-      if constexpr (KPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = packed[0];
+    for (int i = 0; i < LPW; ++i) {
+      const int r = lrow0 + i * RPI;
+      const int p = min(t * KT + r, nkeys - 1);
+      int32_t x;
+      if constexpr (DENSE) {
+        x = p;
       } else {
-        static_assert(KPT == 4, "KPT");
-        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+        const uint32_t bi = fd_div(uint32_t(p), g.div_S);
+        x = cols[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
       }
+      const int32_t off = row_offset(g, grp, x) + (lcp ^ swz<D>(r)) * 8;
+      const int dst = (w * (KT / NW) + i * RPI) * ROWB;
+      load_to_lds16(K + off, kb + dst);
+      load_to_lds16(V + off, vb + dst);
     }
   };
 
   const float c2 = a.scale_log2;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_lds_loads();
   __syncthreads();
+  const int grp16 = lane >> 4, sl = lane & 15;
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const uint16_t* Ks = smem + st * STAGE;
-    const uint16_t* Vs = Ks + KT * RSTR;
-    const uint16_t* Kt = Vs + KT * RSTR;
+    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
+    const unsigned char* kb = smem[st];
+    const unsigned char* vb = smem[st] + TILE;
     f32x16 sacc[KSUB], dpacc[KSUB];
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
@@ -431,9 +390,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a)
       }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const int ro = (kk * 32 + l32) * RSTR + s * 16 + half * 8;
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + ro));
-        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + ro));
+        const int o = tile_off<D>(kk * 32 + l32, 2 * s + half);
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + o));
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + o));
         sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kk], 0, 0, 0);
         dpacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[s], dpacc[kk], 0, 0, 0);
       }
@@ -458,16 +417,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_bf16_kernel(AttnParams a)
       for (int e = 0; e < 4; ++e)
         sw[e] = pack_bf16x2(dpacc[kk][g0 + 2 * e], dpacc[kk][g0 + 2 * e + 1]);
       const bf16x8 sb = as_bf16x8(sw);
+      const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int ro = (dt * 32 + l32) * TSTR + ks * 16 + half * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(Kt + ro);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(Kt + ro + 8);
+        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
+        const int bo = (sl & 1) * 8;
+        const u32x2 lo = lds_read_tr16(kb + tile_off<D>(key0, c) + bo);
+        const u32x2 hi = lds_read_tr16(kb + tile_off<D>(key0 + 8, c) + bo);
         dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dqacc[dt], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile(st ^ 1);
+    wait_lds_loads();
     __syncthreads();
   }
   if (qvalid) {
@@ -660,8 +621,7 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
 template <int D, bool DENSE, typename GT>
 static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
-  // staging splits need an even number of rows per thread: 4 waves at d = 128, 2 at 64
-  constexpr int NWK = D == 128 ? 4 : 2;
+  constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
@@ -671,7 +631,7 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
 template <int D, bool DENSE, typename GT>
 static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
-  constexpr int KSUB = D == 128 ? 1 : 2;
+  constexpr int KSUB = 2;
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;

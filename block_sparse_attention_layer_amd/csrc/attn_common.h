@@ -89,4 +89,45 @@ __device__ __forceinline__ void list_range(const Geom& g, const int32_t* ptr, in
   *len = e - s;
 }
 
+// ---------------------------------------------------------------------------------
+// Row-major bf16 tiles in LDS, filled by direct global->LDS loads.
+//
+// A tile row holds one token's D values (D*2 bytes, 16-byte chunks).  Chunk c of row r
+// is stored at chunk position c ^ swz(r).  The swizzle permutes the chunks of every row
+// so that (1) 16 consecutive rows read at one chunk position (MFMA operands via
+// ds_read_b128) hit 16 different 4-bank groups, and (2) a 4-row x 4-chunk patch (the
+// transposing ds_read_b64_tr_b16 of 16 lanes) also covers all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset of chunk c of row r inside a tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * (D * 2) + 16 * (c ^ swz<D>(r));
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+// One wave instruction copies 64 x 16 bytes from global memory straight into the LDS
+// range [dst, dst + 1024); lane L's chunk lands at dst + 16 L.  `dst` must be uniform.
+__device__ __forceinline__ void load_to_lds16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+
+// Transposing LDS read: the 16 lanes of a group each name 8 bytes (4 bf16); lane i of
+// the group receives element i % 4 of the chunks named by lanes i/4, i/4 + 4, i/4 + 8
+// and i/4 + 12 (in that order).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Wait until this wave's direct-to-LDS loads have landed.
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 }  // namespace vmoba

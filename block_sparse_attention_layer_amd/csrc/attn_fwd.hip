@@ -22,19 +22,19 @@
 namespace vmoba {
 
 template <int D, int NW, int KSUB, bool DENSE>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
   constexpr int QT = NW * 32;
   constexpr int KT = KSUB * 32;
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int KPT = KT * CH / NT;         // keys staged per thread
-  static_assert(KT * CH % NT == 0 && NT % CH == 0, "staging split");
-  static_assert(KPT % 2 == 0, "V^T staging packs key pairs");
-  constexpr int KSTR = D + 8;               // K row stride (bf16)
-  constexpr int VSTR = KT + 4;              // V^T row stride (bf16)
-  constexpr int STAGE = KT * KSTR + D * VSTR;
+  constexpr int ROWB = D * 2;                // bytes per tile row
+  constexpr int RPI = 1024 / ROWB;           // tile rows per wave load instruction
+  constexpr int LPW = KT / (NW * RPI);       // load instructions per wave per tensor
+  static_assert(KT % (NW * RPI) == 0, "tile rows split over waves");
+  constexpr int TILE = KT * ROWB;            // bytes of one K or V tile
+  // lazy rescale: keep the running max until a score exceeds it by 2^8 in exp2 units
+  constexpr float kRescaleLog2 = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t scratch[NW];
 
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
 
-  // key stream
+  // key stream: compacted block list, then each listed block's base token
   int nkeys;
   if constexpr (DENSE) {
     nkeys = g.L;
@@ -64,18 +64,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
     list_range(g, a.row_ptr, grp, iblk, &start, &len);
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
+    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    __syncthreads();
     nkeys = kept * g.S;
   }
   const int ntiles = (nkeys + KT - 1) / KT;
 
-  // this lane's query
+  // this lane's query, Q fragments in registers (B operand of S^T = K Q^T)
   const int qlim = DENSE ? g.L : g.S;
   const int rq = qt * QT + w * 32 + l32;
   const bool qvalid = rq < qlim;
   const int rqc = qvalid ? rq : 0;
   const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
   const int32_t qoff = row_offset(g, grp, xq);
-
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -86,71 +87,45 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // staging role
-  const int c = tid % CH, kg = tid / CH;
-  u32x4 kreg[KPT], vreg[KPT];
-
-  auto load_tile = [&](int t) {
+  // loader role: this lane fetches chunk (lane % CPR) ^ swz(row) of LPW rows per tensor
+  constexpr int CPR = D / 8;
+  const int lrow0 = w * (KT / NW) + lane / CPR;   // + i * RPI
+  const int lcp = lane % CPR;
+  auto issue_tile = [&](int t, int st) {
+    unsigned char* kb = smem[st];
+    unsigned char* vb = smem[st] + TILE;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int p = t * KT + kg * KPT + u;
-      const bool ok = p < nkeys;
-      const int pc = ok ? p : 0;
-      const int32_t x = DENSE ? pc : stream_token(g, cols, uint32_t(pc));
-      const int32_t off = row_offset(g, grp, x) + c * 8;
-      u32x4 kk = *reinterpret_cast<const u32x4*>(K + off);
-      u32x4 vv = *reinterpret_cast<const u32x4*>(V + off);
-      if (!ok) {
-        kk = u32x4{0u, 0u, 0u, 0u};
-        vv = u32x4{0u, 0u, 0u, 0u};
-      }
-      kreg[u] = kk;
-      vreg[u] = vv;
-    }
-  };
-  auto store_tile = [&](int st) {
-    uint16_t* Ks = smem + st * STAGE;
-    uint16_t* Vt = Ks + KT * KSTR;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      *reinterpret_cast<u32x4*>(Ks + (kg * KPT + u) * KSTR + c * 8) = kreg[u];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t packed[KPT / 2];
-#pragma unroll
-      for (int u = 0; u < KPT; u += 2) {
-        const uint32_t lo = (vreg[u][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        const uint32_t hi = (vreg[u + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        packed[u / 2] = lo | (hi << 16);
-      }
-      uint16_t* dst = Vt + (c * 8 + e) * VSTR + kg * KPT;
-      if constexpr (KPT == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = packed[0];
-      } else if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{packed[0], packed[1]};
+    for (int i = 0; i < LPW; ++i) {
+      const int r = lrow0 + i * RPI;
+      const int p = t * KT + r;
+      const int pc = p < nkeys ? p : nkeys - 1;   // ragged end: repeat the last key (masked)
+      int32_t x;
+      if constexpr (DENSE) {
+        x = pc;
       } else {
-#pragma unroll
-        for (int u = 0; u < KPT / 2; u += 4)
-          *reinterpret_cast<u32x4*>(dst + 2 * u) =
-              u32x4{packed[u], packed[u + 1], packed[u + 2], packed[u + 3]};
+        const uint32_t bi = fd_div(uint32_t(pc), g.div_S);
+        x = cols[bi] + block_offset(g, uint32_t(pc) - bi * uint32_t(g.S));
       }
+      const int32_t off = row_offset(g, grp, x) + (lcp ^ swz<D>(r)) * 8;
+      const int dst = (w * (KT / NW) + i * RPI) * ROWB;   // wave-uniform
+      load_to_lds16(K + off, kb + dst);
+      load_to_lds16(V + off, vb + dst);
     }
   };
 
   const float c2 = a.scale_log2;
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  const float thr = kRescaleLog2 / c2;
+  if (ntiles > 0) issue_tile(0, 0);
+  wait_lds_loads();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int st = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const uint16_t* Ks = smem + st * STAGE;
-    const uint16_t* Vt = Ks + KT * KSTR;
+    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
+    const unsigned char* kb = smem[st];
+    const unsigned char* vb = smem[st] + TILE;
 
     // S^T tile: keys along MFMA rows, this lane's query along the column
     f32x16 sacc[KSUB];
@@ -158,14 +133,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
     for (int kt = 0; kt < KSUB; ++kt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
+      const int r = kt * 32 + l32;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 ka = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(Ks + (kt * 32 + l32) * KSTR + s * 16 + half * 8));
+        const bf16x8 ka =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(kb + tile_off<D>(r, 2 * s + half)));
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
       }
     }
-    // mask the ragged end of the stream
     if (t * KT + KT > nkeys) {
 #pragma unroll
       for (int kt = 0; kt < KSUB; ++kt)
@@ -181,9 +156,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    const float moff = m_new * c2;
+    const bool grow = mx > m_run + thr;
+    if (__ballot(grow)) {   // wave-uniform; rare after the first tile
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      m_run = m_new;
+    }
+    const float moff = m_run * c2;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt)
@@ -193,14 +177,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
         sacc[kt][v] = pv;
         psum += pv;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    l_run += psum;
 
-    // O^T += V^T P^T, 16 keys per step
+    // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
+    const int grp16 = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
       const int kt = ks >> 1, g0 = (ks & 1) * 8;
@@ -210,16 +190,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(AttnParams a) {
       pw[2] = pack_bf16x2(sacc[kt][g0 + 4], sacc[kt][g0 + 5]);
       pw[3] = pack_bf16x2(sacc[kt][g0 + 6], sacc[kt][g0 + 7]);
       const bf16x8 pb = as_bf16x8(pw);
+      const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const uint16_t* vp = Vt + (dt * 32 + l32) * VSTR + ks * 16 + half * 4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
+        const int bo = (sl & 1) * 8;
+        const u32x2 lo = lds_read_tr16(vb + tile_off<D>(key0, c) + bo);
+        const u32x2 hi = lds_read_tr16(vb + tile_off<D>(key0 + 8, c) + bo);
         const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile(st ^ 1);
+    wait_lds_loads();
     __syncthreads();
   }
 
