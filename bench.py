@@ -36,7 +36,25 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter scale)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: 2^28 fp32 elements (1 GiB) read and written, 3 times.
+
+    Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its per-dispatch readings give the
+    scale between the counters and algorithmic bytes."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
 
 
 def cpu_baseline(inp, cfg, spec, tau):
@@ -68,6 +86,9 @@ def cpu_baseline(inp, cfg, spec, tau):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the layer "
               f"would shard over heads, see the design notes).", file=sys.stderr)

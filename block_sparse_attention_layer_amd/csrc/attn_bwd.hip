@@ -17,6 +17,8 @@
 //    S^T = K Q^T and dP^T = V dO^T, and K once more transposed for dQ^T += K^T dS^T.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace vmoba {
@@ -80,7 +82,9 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   // per stage: Q tile, dO tile, then 2 x QT floats (lse * log2 e, delta)
   constexpr int STAGE = 2 * TILE + 2 * QT * 4;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][STAGE];
+  // two pipeline stages as separate objects (see the forward kernel)
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
   // V rows of this workgroup's keys (B operands of dP = dO V^T), loaded once
   __shared__ __attribute__((aligned(1024))) unsigned char vtile[NW * 32 * ROWB];
   __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
@@ -88,7 +92,8 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 
   const Geom& g = a.g;
   const int nrow = DENSE ? 1 : g.Nb;
-  int bid = blockIdx.x;
+  int bid = xcd_item(blockIdx.x, g.B * g.Hh, nrow * a.tiles);
+  if (bid < 0) return;
   const int kt = bid % a.tiles;
   bid /= a.tiles;
   const int jblk = bid % nrow;
@@ -166,37 +171,38 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
       return rows_l[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
     }
   };
-  auto issue_tile = [&](int t, int st) {
-    unsigned char* qb = smem[st];
-    unsigned char* ob = smem[st] + TILE;
+  // addresses first, then the loads back to back (no branch join in between)
+  auto issue_tile = [&](int t, unsigned char* sb) {
+    int32_t off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      off[i] = row_offset(g, grp, qtoken(min(t * QT + lrow0 + i * RPI, nq - 1)));
+    const int32_t xl = qtoken(min(t * QT + l32, nq - 1));
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = lrow0 + i * RPI;
-      const int p = min(t * QT + r, nq - 1);   // padding rows repeat the last query
-      const int32_t off = row_offset(g, grp, qtoken(p)) + (lcp ^ swz<D>(r)) * 8;
+      const int32_t o = off[i] + (lcp ^ swz<D>(r)) * 8;
       const int dst = (w * (QT / NW) + i * RPI) * ROWB;
-      load_to_lds16(Q + off, qb + dst);
-      load_to_lds16(dO + off, ob + dst);
+      load_to_lds16(Q + o, sb + dst);
+      load_to_lds16(dO + o, sb + TILE + dst);
     }
     if (w == 0) {   // lanes 0-31: lse of the tile's queries; lanes 32-63: delta
-      const int p = min(t * QT + l32, nq - 1);
-      const int32_t x = qtoken(p);
-      const float* src = half ? dl_g + x : lse_g + x;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(smem[st] + 2 * TILE), 4, 0, 0);
+      const float* src = half ? dl_g + xl : lse_g + xl;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(sb + 2 * TILE), 4, 0, 0);
     }
   };
 
   const float c2 = a.scale_log2;
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_lds_loads();
-  __syncthreads();
   const int grp16 = lane >> 4, sl = lane & 15;
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
-    const unsigned char* qb = smem[st];
-    const unsigned char* ob = smem[st] + TILE;
-    const float* lse_s = reinterpret_cast<const float*>(smem[st] + 2 * TILE);
+  auto step = [&](auto STc, int t) {
+    constexpr int ST = decltype(STc)::value;
+    __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
+    unsigned char* const cur = ST ? stage1 : stage0;
+    unsigned char* const nxt = ST ? stage0 : stage1;
+    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    const unsigned char* qb = cur;
+    const unsigned char* ob = cur + TILE;
+    const float* lse_s = reinterpret_cast<const float*>(cur + 2 * TILE);
     const float* dl_s = lse_s + QT;
 
     f32x16 sacc, dpacc;
@@ -216,6 +222,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
       dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb16, dpacc, 0, 0, 0);
     }
     // sacc[v]: query 8*(v/4) + 4*half + v%4 of the tile; key = this lane
+    __builtin_amdgcn_sched_barrier(0);   // bound the live range of the LSE/delta reads
     const bool ragged = t * QT + QT > nq;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -241,7 +248,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
         pw[e] = pack_bf16x2(sacc[g0 + 2 * e], sacc[g0 + 2 * e + 1]);
         sw[e] = pack_bf16x2(dpacc[g0 + 2 * e], dpacc[g0 + 2 * e + 1]);
       }
-      const bf16x8 pb = as_bf16x8(pw), sb = as_bf16x8(sw);
+      const bf16x8 pb = as_bf16x8(pw), sbf = as_bf16x8(sw);
       const int q0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
@@ -253,12 +260,24 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
         dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]}), pb, dvacc[dt], 0, 0, 0);
         dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sb, dkacc[dt], 0, 0, 0);
+            as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sbf, dkacc[dt], 0, 0, 0);
       }
     }
     wait_lds_loads();
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (ntiles > 0) issue_tile(0, stage0);
+  wait_lds_loads();
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(S0{}, t);
+    step(S1{}, t + 1);
   }
+  if (t < ntiles) step(S0{}, t);
 
   if (kvalid) {
 #pragma unroll
@@ -289,13 +308,15 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   static_assert(KT % (NW * RPI) == 0, "tile rows split over waves");
   constexpr int TILE = KT * ROWB;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
   const int rows = DENSE ? 1 : g.Nb;
-  int bid = blockIdx.x;
+  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
+  if (bid < 0) return;
   const int qt = bid % a.tiles;
   bid /= a.tiles;
   const int iblk = bid % rows;
@@ -349,37 +370,39 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int CPR = D / 8;
   const int lrow0 = w * (KT / NW) + lane / CPR;
   const int lcp = lane % CPR;
-  auto issue_tile = [&](int t, int st) {
-    unsigned char* kb = smem[st];
-    unsigned char* vb = smem[st] + TILE;
+  // addresses first, then the loads back to back (no branch join in between)
+  auto issue_tile = [&](int t, unsigned char* sb) {
+    int32_t off[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int r = lrow0 + i * RPI;
-      const int p = min(t * KT + r, nkeys - 1);
-      int32_t x;
-      if constexpr (DENSE) {
-        x = p;
-      } else {
+      const int p = min(t * KT + lrow0 + i * RPI, nkeys - 1);
+      int32_t x = p;
+      if constexpr (!DENSE) {
         const uint32_t bi = fd_div(uint32_t(p), g.div_S);
         x = cols[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
       }
-      const int32_t off = row_offset(g, grp, x) + (lcp ^ swz<D>(r)) * 8;
+      off[i] = row_offset(g, grp, x);
+    }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int r = lrow0 + i * RPI;
+      const int32_t o = off[i] + (lcp ^ swz<D>(r)) * 8;
       const int dst = (w * (KT / NW) + i * RPI) * ROWB;
-      load_to_lds16(K + off, kb + dst);
-      load_to_lds16(V + off, vb + dst);
+      load_to_lds16(K + o, sb + dst);
+      load_to_lds16(V + o, sb + TILE + dst);
     }
   };
 
   const float c2 = a.scale_log2;
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_lds_loads();
-  __syncthreads();
   const int grp16 = lane >> 4, sl = lane & 15;
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
-    const unsigned char* kb = smem[st];
-    const unsigned char* vb = smem[st] + TILE;
+  auto step = [&](auto STc, int t) {
+    constexpr int ST = decltype(STc)::value;
+    __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
+    unsigned char* const cur = ST ? stage1 : stage0;
+    unsigned char* const nxt = ST ? stage0 : stage1;
+    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    const unsigned char* kb = cur;
+    const unsigned char* vb = cur + TILE;
     f32x16 sacc[KSUB], dpacc[KSUB];
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
@@ -416,7 +439,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         sw[e] = pack_bf16x2(dpacc[kk][g0 + 2 * e], dpacc[kk][g0 + 2 * e + 1]);
-      const bf16x8 sb = as_bf16x8(sw);
+      const bf16x8 sbf = as_bf16x8(sw);
       const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
@@ -425,12 +448,24 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
         const u32x2 lo = lds_read_tr16(kb + tile_off<D>(key0, c) + bo);
         const u32x2 hi = lds_read_tr16(kb + tile_off<D>(key0 + 8, c) + bo);
         dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sb, dqacc[dt], 0, 0, 0);
+            as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sbf, dqacc[dt], 0, 0, 0);
       }
     }
     wait_lds_loads();
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (ntiles > 0) issue_tile(0, stage0);
+  wait_lds_loads();
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(S0{}, t);
+    step(S1{}, t + 1);
   }
+  if (t < ntiles) step(S0{}, t);
   if (qvalid) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -625,17 +660,19 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
-  attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, GT><<<g.B * g.Hh * rows * a.tiles, NWK * 64, 0, s>>>(a);
+  attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, GT>
+      <<<xcd_grid(g.B * g.Hh, rows * a.tiles), NWK * 64, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT>
 static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
-  constexpr int KSUB = 2;
+  constexpr int KSUB = D == 128 ? 1 : 2;   // staging needs KSUB*32*D/8 to split over 4 waves
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;
-  attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, GT><<<g.B * g.Hh * rows * a.tiles, 256, 0, s>>>(a);
+  attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, GT>
+      <<<xcd_grid(g.B * g.Hh, rows * a.tiles), 256, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>

@@ -35,6 +35,38 @@ struct AttnParams {
   float scale_log2;    // log2(e)/sqrt(d)
 };
 
+// The dispatcher hands workgroup b to XCD b % 8, and each XCD has its own L2; all XCDs
+// share the device-wide Infinity Cache.  Work items are numbered head group by head
+// group, and inside a head group so that neighbouring items share K/V (the tiles of one
+// query block, then neighbouring blocks).  The launch index is mapped so that the 8 XCDs
+// advance through the head groups together (one head group's K/V in the shared cache at
+// a time), each XCD taking one contiguous eighth of the current head group's items.
+// Returns -1 for the padding workgroups of the rounded-up grid (they exit at once).
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_item(int bid, int groups, int per_group) {
+  const int chunk = (per_group + kXcds - 1) / kXcds;
+  const int k = bid / kXcds, x = bid % kXcds;
+  const int grp = k / chunk;
+  const int local = x * chunk + k % chunk;
+  return (grp < groups && local < per_group) ? grp * per_group + local : -1;
+}
+
+inline int xcd_grid(int groups, int per_group) {
+  return groups * kXcds * ((per_group + kXcds - 1) / kXcds);
+}
+
+// Blocks of at most this many tokens get an LDS table of in-block token offsets.
+constexpr int kOffsetTable = 2048;
+
+__device__ __forceinline__ int xcd_item(int bid, int items) {
+  const int per = (items + kXcds - 1) / kXcds;
+  const int item = (bid % kXcds) * per + bid / kXcds;
+  return item < items ? item : -1;
+}
+
+inline int xcd_grid(int items) { return ((items + kXcds - 1) / kXcds) * kXcds; }
+
 // Element offset of token x of head group grp in a [B][L][Hh][D] tensor.
 __device__ __forceinline__ int32_t row_offset(const Geom& g, int grp, int32_t x) {
   const int b = grp / g.Hh, h = grp - b * g.Hh;

@@ -17,12 +17,15 @@
 // with LSE = m/sqrt(d) + ln l.
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 
 namespace vmoba {
 
-template <int D, int NW, int KSUB, bool DENSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16_kernel(AttnParams a) {
+template <int D, int NW, int KSUB, bool DENSE, bool TAB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
   constexpr int QT = NW * 32;
   constexpr int KT = KSUB * 32;
@@ -34,13 +37,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // lazy rescale: keep the running max until a score exceeds it by 2^8 in exp2 units
   constexpr float kRescaleLog2 = 8.0f;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2 * TILE];
-  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  // two pipeline stages as separate objects, so the compiler can tell that reads of one
+  // stage do not depend on the direct-to-LDS loads in flight into the other
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];        // base token of listed blocks
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];      // block_offset(r), r < S
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
   const int rows = DENSE ? 1 : g.Nb;
-  int bid = blockIdx.x;
+  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
+  if (bid < 0) return;
   const int qt = bid % a.tiles;
   bid /= a.tiles;
   const int iblk = bid % rows;
@@ -55,7 +63,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
 
-  // key stream: compacted block list, then each listed block's base token
+  // key stream: compacted block list -> base tokens; offsets of tokens inside a block
   int nkeys;
   if constexpr (DENSE) {
     nkeys = g.L;
@@ -65,6 +73,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
     for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
     __syncthreads();
     nkeys = kept * g.S;
   }
@@ -89,84 +99,86 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // loader role: this lane fetches chunk (lane % CPR) ^ swz(row) of LPW rows per tensor
+  // LDS read offsets of this lane (stage, sub-tile and k-step add immediates)
+  const int grp16 = lane >> 4, sl = lane & 15;
+  const int krow = l32 * ROWB, kswz = swz<D>(l32) ^ half;
+  const int vkey0 = 4 * half + (sl >> 2);
+  const int vc0 = 2 * (grp16 & 1) + ((sl & 3) >> 1);
+  const int vbase_lo = TILE + vkey0 * ROWB + (sl & 1) * 8;
+  const int vsw_lo = swz<D>(vkey0), vsw_hi = swz<D>(vkey0 + 8);
+
+  // loader: this lane fetches chunk (lane % CPR) ^ swz(row) of rows r_i = lrow0 + i*RPI;
+  // the stream position of row i in tile t is t*KT + r_i, tracked as (block, offset)
   constexpr int CPR = D / 8;
-  const int lrow0 = w * (KT / NW) + lane / CPR;   // + i * RPI
+  const int lrow0 = w * (KT / NW) + lane / CPR;
   const int lcp = lane % CPR;
-  auto issue_tile = [&](int t, int st) {
-    unsigned char* kb = smem[st];
-    unsigned char* vb = smem[st] + TILE;
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  // Row addresses are computed first, without divergent branches, and the loads are
+  // issued back to back afterwards: a branch join between one row's load and the next
+  // row's address arithmetic would make the compiler wait for the load in flight.
+  auto issue_tile = [&](int t, unsigned char* smem) {
+    int32_t off[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = min(t * KT + lrow0 + i * RPI, nkeys - 1);   // ragged end repeats
+      int32_t x = p;
+      if constexpr (!DENSE) {
+        const uint32_t pb = fd_div(uint32_t(p), g.div_S);
+        const uint32_t rr = uint32_t(p) - pb * uint32_t(g.S);
+        x = cols[pb] + (TAB ? offtab[rr] : block_offset(g, rr));
+      }
+      off[i] = x;
+    }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = lrow0 + i * RPI;
-      const int p = t * KT + r;
-      const int pc = p < nkeys ? p : nkeys - 1;   // ragged end: repeat the last key (masked)
-      int32_t x;
-      if constexpr (DENSE) {
-        x = pc;
-      } else {
-        const uint32_t bi = fd_div(uint32_t(pc), g.div_S);
-        x = cols[bi] + block_offset(g, uint32_t(pc) - bi * uint32_t(g.S));
-      }
-      const int32_t off = row_offset(g, grp, x) + (lcp ^ swz<D>(r)) * 8;
+      const int32_t o = gbase + off[i] * hstride + (lcp ^ swz<D>(r)) * 8;
       const int dst = (w * (KT / NW) + i * RPI) * ROWB;   // wave-uniform
-      load_to_lds16(K + off, kb + dst);
-      load_to_lds16(V + off, vb + dst);
+      load_to_lds16(K + o, smem + dst);
+      load_to_lds16(V + o, smem + TILE + dst);
     }
   };
 
   const float c2 = a.scale_log2;
   const float thr = kRescaleLog2 / c2;
-  if (ntiles > 0) issue_tile(0, 0);
-  wait_lds_loads();
-  __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, st ^ 1);
-    const unsigned char* kb = smem[st];
-    const unsigned char* vb = smem[st] + TILE;
-
-    // S^T tile: keys along MFMA rows, this lane's query along the column
-    f32x16 sacc[KSUB];
+  // S^T of the tile in stage ST: keys along MFMA rows, this lane's query in the column
+  auto scores = [&](auto STc, f32x16* sacc) {
+    const unsigned char* smem = decltype(STc)::value ? stage1 : stage0;
+    constexpr int SB = 0;
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
-      const int r = kt * 32 + l32;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 ka =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(kb + tile_off<D>(r, 2 * s + half)));
+        // chunk 2s + half of row l32 sits at position (2s) ^ swz(l32) ^ half
+        const int ko = krow + 16 * ((2 * s) ^ kswz);
+        const bf16x8 ka = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(smem + SB + kt * 32 * ROWB + ko));
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
       }
     }
-    if (t * KT + KT > nkeys) {
+  };
+  auto mask_tail = [&](int t, f32x16* sacc) {
 #pragma unroll
-      for (int kt = 0; kt < KSUB; ++kt)
+    for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = t * KT + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key >= nkeys) sacc[kt][v] = -INFINITY;
-        }
-    }
+      for (int v = 0; v < 16; ++v) {
+        const int key = t * KT + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (key >= nkeys) sacc[kt][v] = -INFINITY;
+      }
+  };
+  auto tile_max = [&](const f32x16* sacc) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx > m_run + thr;
-    if (__ballot(grow)) {   // wave-uniform; rare after the first tile
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-      m_run = m_new;
-    }
+    return fmaxf(mx, __shfl_xor(mx, 32));
+  };
+  auto exps = [&](f32x16* sacc) {
     const float moff = m_run * c2;
     float psum = 0.f;
 #pragma unroll
@@ -177,32 +189,84 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         sacc[kt][v] = pv;
         psum += pv;
       }
-    l_run += psum;
-
-    // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
-    const int grp16 = lane >> 4, sl = lane & 15;
+    return psum;
+  };
+  auto rescale_to = [&](float m_new) {
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    m_run = m_new;
+  };
+  // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
+  auto pv_update = [&](auto STc, const f32x16* sacc) {
+    const unsigned char* smem = decltype(STc)::value ? stage1 : stage0;
+    constexpr int SB = 0;
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
       const int kt = ks >> 1, g0 = (ks & 1) * 8;
       u32x4 pw;
-      pw[0] = pack_bf16x2(sacc[kt][g0 + 0], sacc[kt][g0 + 1]);
-      pw[1] = pack_bf16x2(sacc[kt][g0 + 2], sacc[kt][g0 + 3]);
-      pw[2] = pack_bf16x2(sacc[kt][g0 + 4], sacc[kt][g0 + 5]);
-      pw[3] = pack_bf16x2(sacc[kt][g0 + 6], sacc[kt][g0 + 7]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[kt][g0 + 2 * e], sacc[kt][g0 + 2 * e + 1]);
       const bf16x8 pb = as_bf16x8(pw);
-      const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
-        const int bo = (sl & 1) * 8;
-        const u32x2 lo = lds_read_tr16(vb + tile_off<D>(key0, c) + bo);
-        const u32x2 hi = lds_read_tr16(vb + tile_off<D>(key0 + 8, c) + bo);
+        const int c = dt * 4 + vc0;
+        const u32x2 lo = lds_read_tr16(smem + SB + ks * 16 * ROWB + vbase_lo + 16 * (c ^ vsw_lo));
+        const u32x2 hi = lds_read_tr16(smem + SB + ks * 16 * ROWB + vbase_lo + 8 * ROWB +
+                                       16 * (c ^ vsw_hi));
         const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
       }
     }
+  };
+
+  // one tile: FIRST sets the running max from the tile; later tiles keep it unless their
+  // max exceeds it by more than the lazy-rescale margin
+  auto step = [&](auto STc, auto FIRSTc, auto LASTc, int t) {
+    constexpr int ST = decltype(STc)::value;
+    constexpr bool FIRST = decltype(FIRSTc)::value, LAST = decltype(LASTc)::value;
+    if (t + 1 < ntiles) issue_tile(t + 1, ST ? stage0 : stage1);
+    f32x16 sacc[KSUB];
+    scores(STc, sacc);
+    if (LAST && t * KT + KT > nkeys) mask_tail(t, sacc);
+    if constexpr (FIRST) {
+      m_run = tile_max(sacc);
+    } else {
+      const float mx = tile_max(sacc);
+      const bool grow = mx > m_run + thr;
+      if (__ballot(grow)) rescale_to(grow ? mx : m_run);   // wave-uniform; rare
+    }
+    l_run += exps(sacc);
+    pv_update(STc, sacc);
     wait_lds_loads();
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (ntiles > 0) issue_tile(0, stage0);
+  wait_lds_loads();
+  __syncthreads();
+  if (ntiles == 1) {
+    step(S0{}, T_{}, T_{}, 0);
+  } else if (ntiles > 1) {
+    step(S0{}, T_{}, F_{}, 0);
+    int t = 1;
+    for (; t + 1 < ntiles - 1; t += 2) {
+      step(S1{}, F_{}, F_{}, t);
+      step(S0{}, F_{}, F_{}, t + 1);
+    }
+    if (t < ntiles - 1) {
+      step(S1{}, F_{}, F_{}, t);
+      ++t;
+    }
+    if (t & 1) step(S1{}, F_{}, T_{}, t);
+    else step(S0{}, F_{}, T_{}, t);
   }
 
   // finalise
@@ -308,8 +372,11 @@ static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const int qlim = DENSE ? g.L : g.S;
   a.tiles = (qlim + NW * 32 - 1) / (NW * 32);
   const int rows = DENSE ? 1 : g.Nb;
-  const int grid = g.B * g.Hh * rows * a.tiles;
-  attn_fwd_bf16_kernel<D, NW, KSUB, DENSE><<<grid, NW * 64, 0, s>>>(a);
+  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_fwd_bf16_kernel<D, NW, KSUB, DENSE, !DENSE><<<grid, NW * 64, 0, s>>>(a);
+  else
+    attn_fwd_bf16_kernel<D, NW, KSUB, DENSE, false><<<grid, NW * 64, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>

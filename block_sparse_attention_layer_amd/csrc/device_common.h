@@ -21,12 +21,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 of two values, packed lo | hi << 16.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed lo | hi << 16 (one
+// v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

@@ -70,6 +70,7 @@ int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
   const size_t pool = size_t(g.Nb) * g.Nb;
   switch (op) {
     case VMOBA_OP_POOL:
+    case VMOBA_OP_SPARSE_FWD:
     case VMOBA_OP_DENSE_FWD:
       *bytes = 0;
       return VMOBA_OK;
@@ -77,16 +78,9 @@ int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
       // raw block scores, fp32 per head group
       *bytes = align256(groups * pool * sizeof(float));
       return VMOBA_OK;
-    case VMOBA_OP_SPARSE_FWD:
-      // per-head-group row order, longest rows first (launch scheduling)
-      *bytes = align256(groups * g.Nb * sizeof(int32_t));
-      return VMOBA_OK;
     case VMOBA_OP_SPARSE_BWD:
-      // delta = rowsum(dO * O) fp32 [B][Hh][L] + row and column orders
-      *bytes = align256(groups * size_t(g.L) * sizeof(float)) +
-               2 * align256(groups * g.Nb * sizeof(int32_t));
-      return VMOBA_OK;
     case VMOBA_OP_DENSE_BWD:
+      // delta = rowsum(dO * O), fp32 [B][Hh][L]
       *bytes = align256(groups * size_t(g.L) * sizeof(float));
       return VMOBA_OK;
     default:
