@@ -128,6 +128,10 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   const int klim = DENSE ? g.L : g.S;
   const int rk = kt * NW * 32 + w * 32 + l32;
   const bool kvalid = rk < klim;
+  // A wave whose 32 keys all lie past the block's end (the ragged last key tile) only
+  // takes its share of the loads and the barriers; its SIMD's matrix core goes to the
+  // other workgroup's wave.
+  const bool wave_busy = kt * NW * 32 + w * 32 < klim;
   const int rkc = kvalid ? rk : 0;
   const int32_t xk = DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
   const int32_t koff = row_offset(g, grp, xk);
@@ -200,6 +204,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
     unsigned char* const cur = ST ? stage1 : stage0;
     unsigned char* const nxt = ST ? stage0 : stage1;
     if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    if (wave_busy) {
     const unsigned char* qb = cur;
     const unsigned char* ob = cur + TILE;
     const float* lse_s = reinterpret_cast<const float*>(cur + 2 * TILE);
@@ -262,6 +267,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
         dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}), sbf, dkacc[dt], 0, 0, 0);
       }
+    }
     }
     wait_lds_loads();
     __syncthreads();
@@ -349,6 +355,8 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   const int qlim = DENSE ? g.L : g.S;
   const int rq = qt * QT + w * 32 + l32;
   const bool qvalid = rq < qlim;
+  // waves with no valid query only load and synchronise (see the dK/dV kernel)
+  const bool wave_busy = qt * QT + w * 32 < qlim;
   const int rqc = qvalid ? rq : 0;
   const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
   const int32_t qoff = row_offset(g, grp, xq);
@@ -401,6 +409,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     unsigned char* const cur = ST ? stage1 : stage0;
     unsigned char* const nxt = ST ? stage0 : stage1;
     if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    if (wave_busy) {
     const unsigned char* kb = cur;
     const unsigned char* vb = cur + TILE;
     f32x16 sacc[KSUB], dpacc[KSUB];
@@ -450,6 +459,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
         dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sbf, dqacc[dt], 0, 0, 0);
       }
+    }
     }
     wait_lds_loads();
     __syncthreads();

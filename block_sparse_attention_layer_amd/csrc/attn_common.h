@@ -162,4 +162,31 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
 // Wait until this wave's direct-to-LDS loads have landed.
 __device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding (the
+// oldest complete first); the LDS and export counters are not waited on.  s_waitcnt
+// immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (they
+// complete oldest first) and all of its LDS operations have completed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier between the steps of a tile pipeline.  Every wave has already waited
+// for its own loads of the tile about to be read and for its own LDS reads of the stage
+// about to be refilled, so the barrier itself need not drain the direct-to-LDS loads
+// still in flight into other stages (a release fence would wait for all of them).  The
+// acquire fence keeps the LDS reads and the loads issued after the barrier behind it.
+__device__ __forceinline__ void pipeline_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 }  // namespace vmoba

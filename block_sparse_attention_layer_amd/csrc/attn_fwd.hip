@@ -23,7 +23,7 @@
 
 namespace vmoba {
 
-template <int D, int NW, int KSUB, bool DENSE, bool TAB>
+template <int D, int NW, int KSUB, int NS, bool DENSE, bool TAB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -33,17 +33,27 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   constexpr int RPI = 1024 / ROWB;           // tile rows per wave load instruction
   constexpr int LPW = KT / (NW * RPI);       // load instructions per wave per tensor
   static_assert(KT % (NW * RPI) == 0, "tile rows split over waves");
+  static_assert(NS >= 2 && NS <= 4, "stages");
   constexpr int TILE = KT * ROWB;            // bytes of one K or V tile
   // lazy rescale: keep the running max until a score exceeds it by 2^8 in exp2 units
   constexpr float kRescaleLog2 = 8.0f;
 
-  // two pipeline stages as separate objects, so the compiler can tell that reads of one
-  // stage do not depend on the direct-to-LDS loads in flight into the other
+  // Pipeline stages as separate objects, so that the compiler can tell that reading one
+  // stage does not depend on the direct-to-LDS loads in flight into another.
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[NS > 2 ? 2 * TILE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[NS > 3 ? 2 * TILE : 16];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];        // base token of listed blocks
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];      // block_offset(r), r < S
   __shared__ int32_t scratch[NW];
+  auto stage = [&](auto Ic) -> unsigned char* {
+    constexpr int I = decltype(Ic)::value % NS;
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
+  };
 
   const Geom& g = a.g;
   const int rows = DENSE ? 1 : g.Nb;
@@ -73,6 +83,7 @@ void attn_fwd_bf16_kernel(AttnParams a) {
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
     for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: loads of an empty stream
     if constexpr (TAB)
       for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
     __syncthreads();
@@ -84,6 +95,10 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   const int qlim = DENSE ? g.L : g.S;
   const int rq = qt * QT + w * 32 + l32;
   const bool qvalid = rq < qlim;
+  // A wave whose 32 queries all lie past the block's end (the ragged last query tile)
+  // only takes its share of the loads and the barriers: skipping the arithmetic leaves
+  // its SIMD's matrix core to the other workgroup's wave.
+  const bool wave_busy = qt * QT + w * 32 < qlim;
   const int rqc = qvalid ? rq : 0;
   const int32_t xq = DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
   const int32_t qoff = row_offset(g, grp, xq);
@@ -99,7 +114,7 @@ void attn_fwd_bf16_kernel(AttnParams a) {
     for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // LDS read offsets of this lane (stage, sub-tile and k-step add immediates)
+  // LDS read offsets of this lane (sub-tile and k-step add immediates)
   const int grp16 = lane >> 4, sl = lane & 15;
   const int krow = l32 * ROWB, kswz = swz<D>(l32) ^ half;
   const int vkey0 = 4 * half + (sl >> 2);
@@ -107,115 +122,136 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   const int vbase_lo = TILE + vkey0 * ROWB + (sl & 1) * 8;
   const int vsw_lo = swz<D>(vkey0), vsw_hi = swz<D>(vkey0 + 8);
 
-  // loader: this lane fetches chunk (lane % CPR) ^ swz(row) of rows r_i = lrow0 + i*RPI;
-  // the stream position of row i in tile t is t*KT + r_i, tracked as (block, offset)
+  // loader: this lane fetches chunk (lane % CPR) ^ swz(row) of rows lrow0 + i*RPI of the
+  // tile.  Row addresses are computed first, without divergent branches, and the loads
+  // issued back to back afterwards: a branch join between one row's load and the next
+  // row's address arithmetic would make the compiler wait for the load in flight.
+  // Positions past the stream's end repeat its last token (an empty stream reads token
+  // 0), so every tile, also one past the end, is a valid load and the pipeline issues
+  // one tile per step unconditionally.
   constexpr int CPR = D / 8;
   const int lrow0 = w * (KT / NW) + lane / CPR;
   const int lcp = lane % CPR;
   const int32_t hstride = g.Hh * D;
   const int32_t gbase = row_offset(g, grp, 0);
-  // Row addresses are computed first, without divergent branches, and the loads are
-  // issued back to back afterwards: a branch join between one row's load and the next
-  // row's address arithmetic would make the compiler wait for the load in flight.
-  auto issue_tile = [&](int t, unsigned char* smem) {
-    int32_t off[LPW];
+  const int plast = max(nkeys - 1, 0);
+  // element offsets (shared by K and V) of this lane's rows of tile t
+  auto tile_offsets = [&](int t, int32_t (&o)[LPW]) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int p = min(t * KT + lrow0 + i * RPI, nkeys - 1);   // ragged end repeats
+      const int p = min(t * KT + lrow0 + i * RPI, plast);
       int32_t x = p;
       if constexpr (!DENSE) {
         const uint32_t pb = fd_div(uint32_t(p), g.div_S);
         const uint32_t rr = uint32_t(p) - pb * uint32_t(g.S);
         x = cols[pb] + (TAB ? offtab[rr] : block_offset(g, rr));
       }
-      off[i] = x;
+      o[i] = gbase + x * hstride + (lcp ^ swz<D>(lrow0 + i * RPI)) * 8;
     }
+  };
+  auto issue_offsets = [&](const int32_t (&o)[LPW], unsigned char* smem) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int r = lrow0 + i * RPI;
-      const int32_t o = gbase + off[i] * hstride + (lcp ^ swz<D>(r)) * 8;
       const int dst = (w * (KT / NW) + i * RPI) * ROWB;   // wave-uniform
-      load_to_lds16(K + o, smem + dst);
-      load_to_lds16(V + o, smem + TILE + dst);
+      load_to_lds16(K + o[i], smem + dst);
+      load_to_lds16(V + o[i], smem + TILE + dst);
     }
+  };
+  auto issue_tile = [&](int t, unsigned char* smem) {
+    int32_t o[LPW];
+    tile_offsets(t, o);
+    issue_offsets(o, smem);
   };
 
   const float c2 = a.scale_log2;
   const float thr = kRescaleLog2 / c2;
 
-  // S^T of the tile in stage ST: keys along MFMA rows, this lane's query in the column
-  auto scores = [&](auto STc, f32x16* sacc) {
-    const unsigned char* smem = decltype(STc)::value ? stage1 : stage0;
-    constexpr int SB = 0;
-#pragma unroll
-    for (int kt = 0; kt < KSUB; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        // chunk 2s + half of row l32 sits at position (2s) ^ swz(l32) ^ half
-        const int ko = krow + 16 * ((2 * s) ^ kswz);
-        const bf16x8 ka = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(smem + SB + kt * 32 * ROWB + ko));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kt], 0, 0, 0);
-      }
-    }
-  };
-  auto mask_tail = [&](int t, f32x16* sacc) {
+  // K fragments of a tile (A operand of S^T = K Q^T): chunk 2s + half of row l32 sits at
+  // chunk position (2s) ^ swz(l32) ^ half
+  auto load_k = [&](const unsigned char* smem, bf16x8 (&kf)[KSUB][D / 16]) {
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = t * KT + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (key >= nkeys) sacc[kt][v] = -INFINITY;
-      }
+      for (int s = 0; s < D / 16; ++s)
+        kf[kt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            smem + kt * 32 * ROWB + krow + 16 * ((2 * s) ^ kswz)));
   };
-  auto tile_max = [&](const f32x16* sacc) {
+  auto scores = [&](const bf16x8 (&kf)[KSUB][D / 16], f32x16 (&acc)[KSUB]) {
+#pragma unroll
+    for (int kt = 0; kt < KSUB; ++kt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kt][v] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][s], qf[s], acc[kt], 0, 0, 0);
+    }
+  };
+  // keys of the ragged last tile past the stream's end score -inf
+  auto mask_tail = [&](f32x16 (&acc)[KSUB], int t) {
+    if (t * KT + KT > nkeys) {
+#pragma unroll
+      for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = t * KT + kt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key >= nkeys) acc[kt][v] = -INFINITY;
+        }
+    }
+  };
+  // max over the tile's keys of this lane's query: the lane's own 16*KSUB scores, then the
+  // other lane half (lane l ^ 32 holds the other keys of the same query)
+  auto tile_max = [&](const f32x16 (&acc)[KSUB]) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
-    return fmaxf(mx, __shfl_xor(mx, 32));
+      for (int v = 0; v < 16; v += 2) mx = max3f(mx, acc[kt][v], acc[kt][v + 1]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
-  auto exps = [&](f32x16* sacc) {
+  // lazy rescale: keep the running max unless the tile's max exceeds it by the margin
+  // (every lane on the first tile, rarely afterwards)
+  auto maybe_rescale = [&](float mx) {
+    const bool grow = mx > m_run + thr;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // P = exp2(S c2 - m c2), summed into l and packed to bf16 pairs (B operand of O^T += V^T P^T)
+  auto softmax_pack = [&](const f32x16 (&acc)[KSUB], u32x4 (&pw)[2 * KSUB]) {
     const float moff = m_run * c2;
     float psum = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < KSUB; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][v], c2, -moff));
-        sacc[kt][v] = pv;
-        psum += pv;
-      }
-    return psum;
-  };
-  auto rescale_to = [&](float m_new) {
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-    m_run = m_new;
-  };
-  // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
-  auto pv_update = [&](auto STc, const f32x16* sacc) {
-    const unsigned char* smem = decltype(STc)::value ? stage1 : stage0;
-    constexpr int SB = 0;
-#pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
       const int kt = ks >> 1, g0 = (ks & 1) * 8;
-      u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(sacc[kt][g0 + 2 * e], sacc[kt][g0 + 2 * e + 1]);
-      const bf16x8 pb = as_bf16x8(pw);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[kt][g0 + 2 * e], c2, -moff));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[kt][g0 + 2 * e + 1], c2, -moff));
+        psum += p0 + p1;
+        pw[ks][e] = pack_bf16x2(p0, p1);
+      }
+    }
+    l_run += psum;
+  };
+  // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
+  auto pv_update = [&](const unsigned char* smem, const u32x4 (&pw)[2 * KSUB]) {
+#pragma unroll
+    for (int ks = 0; ks < 2 * KSUB; ++ks) {
+      const bf16x8 pb = as_bf16x8(pw[ks]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int c = dt * 4 + vc0;
-        const u32x2 lo = lds_read_tr16(smem + SB + ks * 16 * ROWB + vbase_lo + 16 * (c ^ vsw_lo));
-        const u32x2 hi = lds_read_tr16(smem + SB + ks * 16 * ROWB + vbase_lo + 8 * ROWB +
+        const u32x2 lo = lds_read_tr16(smem + ks * 16 * ROWB + vbase_lo + 16 * (c ^ vsw_lo));
+        const u32x2 hi = lds_read_tr16(smem + ks * 16 * ROWB + vbase_lo + 8 * ROWB +
                                        16 * (c ^ vsw_hi));
         const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[dt], 0, 0, 0);
@@ -223,53 +259,62 @@ void attn_fwd_bf16_kernel(AttnParams a) {
     }
   };
 
-  // one tile: FIRST sets the running max from the tile; later tiles keep it unless their
-  // max exceeds it by more than the lazy-rescale margin
-  auto step = [&](auto STc, auto FIRSTc, auto LASTc, int t) {
+  // Software pipeline over key tiles.  Tile t sits in stage t % NS; tiles up to t + NS - 2
+  // are in flight.  Step t: wait for tile t+1, barrier, refill the stage of tile t-1 with
+  // tile t+NS-1 (its addresses were computed one step earlier), then compute S(t+1) on the matrix cores while the vector unit turns S(t)
+  // into P(t), and finish with O += P(t) V(t).  S(t) itself was computed in step t-1.
+  static_assert(NS == 4, "the step loop is unrolled over four stages");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int32_t noff[LPW];   // offsets of the tile the next step loads
+  auto step = [&](auto STc, int t, f32x16 (&cur)[KSUB], f32x16 (&nxt)[KSUB]) {
     constexpr int ST = decltype(STc)::value;
-    constexpr bool FIRST = decltype(FIRSTc)::value, LAST = decltype(LASTc)::value;
-    if (t + 1 < ntiles) issue_tile(t + 1, ST ? stage0 : stage1);
-    f32x16 sacc[KSUB];
-    scores(STc, sacc);
-    if (LAST && t * KT + KT > nkeys) mask_tail(t, sacc);
-    if constexpr (FIRST) {
-      m_run = tile_max(sacc);
-    } else {
-      const float mx = tile_max(sacc);
-      const bool grow = mx > m_run + thr;
-      if (__ballot(grow)) rescale_to(grow ? mx : m_run);   // wave-uniform; rare
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lds<(NS - 3) * 2 * LPW>();   // this wave's loads of tile t+1 have landed
+    pipeline_barrier();
+    issue_offsets(noff, stage(std::integral_constant<int, ST + NS - 1>{}));
+    tile_offsets(t + NS, noff);   // the next step's loads; the lookups finish meanwhile
+    if (wave_busy) {
+      bf16x8 kf[KSUB][D / 16];
+      load_k(stage(std::integral_constant<int, ST + 1>{}), kf);
+      mask_tail(cur, t);
+      maybe_rescale(tile_max(cur));
+      u32x4 pw[2 * KSUB];
+      scores(kf, nxt);
+      softmax_pack(cur, pw);
+      pv_update(stage(STc), pw);
     }
-    l_run += exps(sacc);
-    pv_update(STc, sacc);
-    wait_lds_loads();
-    __syncthreads();
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  if (ntiles > 0) issue_tile(0, stage0);
-  wait_lds_loads();
-  __syncthreads();
-  if (ntiles == 1) {
-    step(S0{}, T_{}, T_{}, 0);
-  } else if (ntiles > 1) {
-    step(S0{}, T_{}, F_{}, 0);
-    int t = 1;
-    for (; t + 1 < ntiles - 1; t += 2) {
-      step(S1{}, F_{}, F_{}, t);
-      step(S0{}, F_{}, F_{}, t + 1);
-    }
-    if (t < ntiles - 1) {
-      step(S1{}, F_{}, F_{}, t);
-      ++t;
-    }
-    if (t & 1) step(S1{}, F_{}, T_{}, t);
-    else step(S0{}, F_{}, T_{}, t);
+  // prologue: tiles 0 .. NS-2 in flight, S(0)
+  issue_tile(0, stage0);
+  issue_tile(1, stage1);
+  issue_tile(2, stage2);
+  tile_offsets(NS - 1, noff);
+  f32x16 sa[KSUB], sb[KSUB];
+  wait_vmcnt_lds<(NS - 2) * 2 * LPW>();
+  pipeline_barrier();
+  if (wave_busy) {
+    bf16x8 kf[KSUB][D / 16];
+    load_k(stage0, kf);
+    scores(kf, sa);
   }
+  int t = 0;
+  for (; t + NS <= ntiles; t += NS) {
+    step(I0{}, t, sa, sb);
+    step(I1{}, t + 1, sb, sa);
+    step(I2{}, t + 2, sa, sb);
+    step(I3{}, t + 3, sb, sa);
+  }
+  if (t < ntiles) step(I0{}, t, sa, sb);
+  if (t + 1 < ntiles) step(I1{}, t + 1, sb, sa);
+  if (t + 2 < ntiles) step(I2{}, t + 2, sa, sb);
 
-  // finalise
+  // finalise; the loads of the tiles past the end must land before the workgroup's LDS
+  // is released
+  wait_vmcnt_lds<0>();
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const bool empty = nkeys == 0;
   const float inv = empty ? 0.f : 1.0f / l_tot;
@@ -366,7 +411,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams a) {
   }
 }
 
-template <int D, int NW, int KSUB, bool DENSE>
+template <int D, int NW, int KSUB, int NS, bool DENSE>
 static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const Geom& g = a.g;
   const int qlim = DENSE ? g.L : g.S;
@@ -374,9 +419,9 @@ static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const int rows = DENSE ? 1 : g.Nb;
   const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_fwd_bf16_kernel<D, NW, KSUB, DENSE, !DENSE><<<grid, NW * 64, 0, s>>>(a);
+    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, !DENSE><<<grid, NW * 64, 0, s>>>(a);
   else
-    attn_fwd_bf16_kernel<D, NW, KSUB, DENSE, false><<<grid, NW * 64, 0, s>>>(a);
+    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, false><<<grid, NW * 64, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>
@@ -405,12 +450,13 @@ int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
   a.scale = 1.0f / sqrtf(float(g.D));
   a.scale_log2 = kLog2e * a.scale;
   if (g.dtype == VMOBA_BF16) {
+    // 32-key tiles, 4 stages: three tiles of loads in flight behind the one in use
     if (g.D == 128) {
-      if (dense) launch_fwd_bf16<128, 4, 2, true>(a, s);
-      else launch_fwd_bf16<128, 4, 2, false>(a, s);
+      if (dense) launch_fwd_bf16<128, 4, 1, 4, true>(a, s);
+      else launch_fwd_bf16<128, 4, 1, 4, false>(a, s);
     } else {
-      if (dense) launch_fwd_bf16<64, 4, 2, true>(a, s);
-      else launch_fwd_bf16<64, 4, 2, false>(a, s);
+      if (dense) launch_fwd_bf16<64, 4, 2, 4, true>(a, s);
+      else launch_fwd_bf16<64, 4, 2, 4, false>(a, s);
     }
   } else {
     if (g.D == 128) {
