@@ -334,6 +334,327 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// d = 128 on v_mfma_f32_16x16x32_bf16: each wave owns M sub-tiles of 16 queries, so a
+// workgroup covers 64*M queries (a whole 192-token block at M = 3).  Every K and V^T
+// fragment read from LDS feeds M products, and each staged K/V tile serves 64*M queries,
+// which cuts both the LDS reads per pair and the tile loads per query against 32 queries
+// per wave.
+//
+// Per 32-key tile and wave: S^T = K Q^T as 2 key sub-tiles x M query sub-tiles x 4 d-steps
+// (A = K rows from LDS, B = this wave's Q columns in registers); the accumulator gives lane
+// l the query l % 16 of each sub-tile and keys 4*(l/16) + 0..3 of each key sub-tile.  The
+// row max reduces over the lane's 8 values and then over the four 16-lane groups (two
+// permlane swaps).  P stays in registers as the B operand of O^T += V^T P^T with its k order
+// permuted to the accumulator layout (k position 8g + e is key 4g + e for e < 4 and
+// 16 + 4g + e - 4 otherwise); the V^T operand comes from two transposing reads that follow
+// the same permutation.
+//
+// LDS tiles: row r holds one token (256 bytes, 16 chunks of 16 bytes).  K chunk c of row r
+// sits at position c ^ (r & 15), so the 16 rows of a K fragment read hit 16 different bank
+// groups; V chunk c of row r sits at c ^ 2 (r & 7), so the 8 rows x 32 bytes of a
+// half-wave's transposing read cover all 64 banks.
+template <int M, int NS, bool DENSE, bool TAB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd16_bf16_kernel(AttnParams a) {
+  constexpr int D = 128, NW = 4, NT = 256;
+  constexpr int QW = 16 * M;                 // queries per wave
+  constexpr int QT = NW * QW;                // queries per workgroup
+  constexpr int KT = 32;                     // keys per tile
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = KT * ROWB;            // bytes of one K or V tile
+  constexpr int LPW = KT / (NW * 4);         // load instructions per wave per tensor
+  static_assert(NS == 4, "the step loop is unrolled over four stages");
+  constexpr float kRescaleLog2 = 8.0f;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
+  __shared__ int32_t scratch[NW];
+  auto stage = [&](auto Ic) -> unsigned char* {
+    constexpr int I = decltype(Ic)::value % NS;
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
+  };
+
+  const Geom& g = a.g;
+  const int rows = DENSE ? 1 : g.Nb;
+  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
+  if (bid < 0) return;
+  const int qt = bid % a.tiles;
+  bid /= a.tiles;
+  const int iblk = bid % rows;
+  const int grp = bid / rows;
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  uint16_t* __restrict__ O = static_cast<uint16_t*>(a.out);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g16 = lane >> 4, i16 = lane & 15;
+
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, cols, scratch);
+    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: loads of an empty stream
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+    __syncthreads();
+    nkeys = kept * g.S;
+  }
+  const int ntiles = (nkeys + KT - 1) / KT;
+
+  // this lane's query in each sub-tile; Q fragments (B operands) in registers
+  const int qlim = DENSE ? g.L : g.S;
+  const int qbase = qt * QT + w * QW;
+  const bool wave_busy = qbase < qlim;   // otherwise: loads and barriers only
+  auto query_token = [&](int m) -> int32_t {   // token of this lane's query in sub-tile m
+    const int rq = qbase + m * 16 + i16;
+    const int rqc = rq < qlim ? rq : 0;
+    return DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  };
+  bf16x8 qf[M][D / 32];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int32_t qoff = row_offset(g, grp, query_token(m));
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      qf[m][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + qoff + s * 32 + g16 * 8));
+  }
+
+  f32x4 oacc[M][D / 16];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) oacc[m][ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[M], l_run[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    m_run[m] = -INFINITY;
+    l_run[m] = 0.f;
+  }
+
+  // loader: one instruction moves 4 rows; lane L fills row L/16 at chunk position L % 16
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  const int plast = max(nkeys - 1, 0);
+  int kchunk[LPW], vchunk[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = w * (KT / NW) + i * 4 + g16;
+    kchunk[i] = (i16 ^ (r & 15)) * 8;
+    vchunk[i] = (i16 ^ (2 * (r & 7))) * 8;
+  }
+  auto tile_offsets = [&](int t, int32_t (&o)[LPW]) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int p = min(t * KT + w * (KT / NW) + i * 4 + g16, plast);
+      int32_t x = p;
+      if constexpr (!DENSE) {
+        const uint32_t pb = fd_div(uint32_t(p), g.div_S);
+        const uint32_t rr = uint32_t(p) - pb * uint32_t(g.S);
+        x = cols[pb] + (TAB ? offtab[rr] : block_offset(g, rr));
+      }
+      o[i] = gbase + x * hstride;
+    }
+  };
+  auto issue_offsets = [&](const int32_t (&o)[LPW], unsigned char* smem) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int dst = (w * (KT / NW) + i * 4) * ROWB;   // wave-uniform
+      load_to_lds16(K + o[i] + kchunk[i], smem + dst);
+      load_to_lds16(V + o[i] + vchunk[i], smem + TILE + dst);
+    }
+  };
+  auto issue_tile = [&](int t, unsigned char* smem) {
+    int32_t o[LPW];
+    tile_offsets(t, o);
+    issue_offsets(o, smem);
+  };
+
+  // LDS read offsets: K fragment (key sub-tile ks, d-step s) of lane l is row ks*16 + l%16,
+  // chunk 4s + l/16; the V^T reads of lane l name row 4*(l/16) + (l%16)/4 (+16 for keys
+  // 16..31) and the 8 bytes at d = 16 dsub + 4 (l % 4)
+  const int krd = i16 * ROWB;
+  const int vrow = 4 * g16 + (i16 >> 2);
+  const int vrd = TILE + vrow * ROWB + 8 * (i16 & 1);
+  const int vsw = 2 * (vrow & 7);
+  const int vc = (i16 & 3) >> 1;
+
+  const float c2 = a.scale_log2;
+  const float thr = kRescaleLog2 / c2;
+
+  auto compute = [&](const unsigned char* sm, int t) {
+    f32x4 sacc[2][M];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < M; ++m) sacc[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ka[2][D / 32];   // all K fragments of the tile first: one LDS wait, not eight
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        ka[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            sm + ks * 16 * ROWB + krd + 16 * ((4 * s + g16) ^ i16)));
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their products
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks][s], qf[m][s], sacc[ks][m],
+                                                                0, 0, 0);
+    // V^T fragments, issued once the K fragments are dead: the compiler waits for every
+    // LDS read before the first use of a transposing read's result, so they must be in
+    // flight long before the products that need them
+    bf16x8 va[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int o = vrd + 16 * ((2 * ds + vc) ^ vsw);
+      const u32x2 lo = lds_read_tr16(sm + o);
+      const u32x2 hi = lds_read_tr16(sm + o + 16 * ROWB);
+      va[ds] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t * KT + KT > nkeys) {   // ragged last tile: keys past the end score -inf
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t * KT + ks * 16 + 4 * g16 + i >= nkeys) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) sacc[ks][m][i] = -INFINITY;
+          }
+    }
+    // per query: max over the lane's 8 scores, then over the four 16-lane groups
+    float mx[M];
+    bool any = false;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = max3f(sacc[0][m][0], sacc[0][m][1], sacc[0][m][2]);
+      v = max3f(v, sacc[0][m][3], sacc[1][m][0]);
+      v = max3f(v, sacc[1][m][1], sacc[1][m][2]);
+      v = __builtin_elementwise_maximum(v, sacc[1][m][3]);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+      v = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+      mx[m] = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      any |= mx[m] > m_run[m] + thr;
+    }
+    // lazy rescale (wave-uniform): every sub-tile on the first tile, rarely afterwards
+    if (__ballot(any)) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float m_new = mx[m] > m_run[m] + thr ? mx[m] : m_run[m];
+        const float alpha = __builtin_amdgcn_exp2f((m_run[m] - m_new) * c2);
+        l_run[m] *= alpha;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) oacc[m][ds] *= alpha;
+        m_run[m] = m_new;
+      }
+    }
+    // P = exp2(S c2 - m c2), packed in the permuted k order
+    u32x4 pw[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float moff = m_run[m] * c2;
+      float p[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          p[ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -moff));
+      l_run[m] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                  ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      pw[m] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        oacc[m][ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ds], as_bf16x8(pw[m]),
+                                                              oacc[m][ds], 0, 0, 0);
+  };
+
+  // pipeline: tile t in stage t % 4, tiles t+1, t+2 in flight while t is computed
+  int32_t noff[LPW];
+  auto step = [&](auto STc, int t) {
+    constexpr int ST = decltype(STc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lds<(NS - 2) * 2 * LPW>();   // this wave's loads of tile t have landed
+    pipeline_barrier();
+    issue_offsets(noff, stage(std::integral_constant<int, ST + NS - 1>{}));
+    tile_offsets(t + NS, noff);
+    if (wave_busy) compute(stage(STc), t);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  issue_tile(0, stage0);
+  issue_tile(1, stage1);
+  issue_tile(2, stage2);
+  tile_offsets(NS - 1, noff);
+  int t = 0;
+  for (; t + NS <= ntiles; t += NS) {
+    step(I0{}, t);
+    step(I1{}, t + 1);
+    step(I2{}, t + 2);
+    step(I3{}, t + 3);
+  }
+  if (t < ntiles) step(I0{}, t);
+  if (t + 1 < ntiles) step(I1{}, t + 1);
+  if (t + 2 < ntiles) step(I2{}, t + 2);
+  // the loads of the tiles past the end must land before the LDS is released
+  wait_vmcnt_lds<0>();
+
+  // finalise: row sums over the four lane groups, O / l in natural token order, LSE
+  const bool empty = nkeys == 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float l = l_run[m];
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l),
+                                                      false, false);
+    l = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
+                                                      false, false);
+    l = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    const float inv = empty ? 0.f : 1.0f / l;
+    if (qbase + m * 16 + i16 < qlim) {
+      const int32_t xq = query_token(m);
+      const int32_t qoff = row_offset(g, grp, xq);
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) {
+        u32x2 out;
+        out[0] = pack_bf16x2(oacc[m][ds][0] * inv, oacc[m][ds][1] * inv);
+        out[1] = pack_bf16x2(oacc[m][ds][2] * inv, oacc[m][ds][3] * inv);
+        *reinterpret_cast<u32x2*>(O + qoff + ds * 16 + 4 * g16) = out;
+      }
+      if (g16 == 0)
+        a.lse[size_t(grp) * g.L + xq] = empty ? -INFINITY : m_run[m] * a.scale + logf(l);
+    }
+  }
+}
+
 // fp32 instance (VALU, one query per lane): the plain online-softmax recurrence over the
 // same key stream, for fp32 inputs.
 template <int D, bool DENSE>
@@ -424,6 +745,19 @@ static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
     attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, false><<<grid, NW * 64, 0, s>>>(a);
 }
 
+template <int M, bool DENSE>
+static void launch_fwd16_bf16(AttnParams& a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int qlim = DENSE ? g.L : g.S;
+  a.tiles = (qlim + 64 * M - 1) / (64 * M);
+  const int rows = DENSE ? 1 : g.Nb;
+  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_fwd16_bf16_kernel<M, 4, DENSE, !DENSE><<<grid, 256, 0, s>>>(a);
+  else
+    attn_fwd16_bf16_kernel<M, 4, DENSE, false><<<grid, 256, 0, s>>>(a);
+}
+
 template <int D, bool DENSE>
 static void launch_fwd_f32(AttnParams& a, hipStream_t s) {
   const Geom& g = a.g;
@@ -452,8 +786,16 @@ int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
   if (g.dtype == VMOBA_BF16) {
     // 32-key tiles, 4 stages: three tiles of loads in flight behind the one in use
     if (g.D == 128) {
-      if (dense) launch_fwd_bf16<128, 4, 1, 4, true>(a, s);
-      else launch_fwd_bf16<128, 4, 1, 4, false>(a, s);
+      // 48 queries per wave when 192-query tiles pad no more than 128-query ones
+      const int qlim = dense ? g.L : g.S;
+      const bool m3 = (qlim + 191) / 192 * 192 <= (qlim + 127) / 128 * 128;
+      if (m3) {
+        if (dense) launch_fwd16_bf16<3, true>(a, s);
+        else launch_fwd16_bf16<3, false>(a, s);
+      } else {
+        if (dense) launch_fwd_bf16<128, 4, 1, 4, true>(a, s);
+        else launch_fwd_bf16<128, 4, 1, 4, false>(a, s);
+      }
     } else {
       if (dense) launch_fwd_bf16<64, 4, 2, 4, true>(a, s);
       else launch_fwd_bf16<64, 4, 2, 4, false>(a, s);
