@@ -69,7 +69,7 @@ __device__ __forceinline__ void store4(GT* dst, float a, float b, float c, float
 
 // ---------------------------------------------------------------------------------
 // dK, dV: one wave per 32 keys, query stream from the column list of the key block.
-template <int D, int NW, bool DENSE, typename GT>
+template <int D, int NW, bool DENSE, bool TAB, typename GT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -88,6 +88,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   // V rows of this workgroup's keys (B operands of dP = dO V^T), loaded once
   __shared__ __attribute__((aligned(1024))) unsigned char vtile[NW * 32 * ROWB];
   __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];   // block_offset(r), r < S
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
@@ -119,6 +120,9 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
     const int kept = compact_list<NT>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, rows_l, scratch);
     for (int i = tid; i < kept; i += NT) rows_l[i] = block_base(g, uint32_t(rows_l[i]));
+    if (kept == 0 && tid == 0) rows_l[0] = 0;   // token 0: address of an empty stream
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
     __syncthreads();
     nq = kept * g.S;
   }
@@ -167,33 +171,43 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int CPR = D / 8;
   const int lrow0 = w * (QT / NW) + lane / CPR;
   const int lcp = lane % CPR;
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  const int plast = max(nq - 1, 0);   // positions past the end repeat the last query
   auto qtoken = [&](int p) -> int32_t {
     if constexpr (DENSE) {
       return p;
     } else {
       const uint32_t bi = fd_div(uint32_t(p), g.div_S);
-      return rows_l[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
+      const uint32_t r = uint32_t(p) - bi * uint32_t(g.S);
+      return rows_l[bi] + (TAB ? offtab[r] : block_offset(g, r));
     }
   };
-  // addresses first, then the loads back to back (no branch join in between)
-  auto issue_tile = [&](int t, unsigned char* sb) {
-    int32_t off[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      off[i] = row_offset(g, grp, qtoken(min(t * QT + lrow0 + i * RPI, nq - 1)));
-    const int32_t xl = qtoken(min(t * QT + l32, nq - 1));
+  // element offsets of this lane's Q/dO rows of tile t, and the token of its LSE/delta
+  auto tile_offsets = [&](int t, int32_t (&o)[LPW], int32_t& xl) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = lrow0 + i * RPI;
-      const int32_t o = off[i] + (lcp ^ swz<D>(r)) * 8;
+      o[i] = gbase + qtoken(min(t * QT + r, plast)) * hstride + (lcp ^ swz<D>(r)) * 8;
+    }
+    xl = qtoken(min(t * QT + l32, plast));
+  };
+  auto issue_offsets = [&](const int32_t (&o)[LPW], int32_t xl, unsigned char* sb) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
       const int dst = (w * (QT / NW) + i * RPI) * ROWB;
-      load_to_lds16(Q + o, sb + dst);
-      load_to_lds16(dO + o, sb + TILE + dst);
+      load_to_lds16(Q + o[i], sb + dst);
+      load_to_lds16(dO + o[i], sb + TILE + dst);
     }
     if (w == 0) {   // lanes 0-31: lse of the tile's queries; lanes 32-63: delta
       const float* src = half ? dl_g + xl : lse_g + xl;
       __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(sb + 2 * TILE), 4, 0, 0);
     }
+  };
+  auto issue_tile = [&](int t, unsigned char* sb) {
+    int32_t o[LPW], xl;
+    tile_offsets(t, o, xl);
+    issue_offsets(o, xl, sb);
   };
 
   const float c2 = a.scale_log2;
@@ -228,7 +242,6 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
     }
     // sacc[v]: query 8*(v/4) + 4*half + v%4 of the tile; key = this lane
     __builtin_amdgcn_sched_barrier(0);   // bound the live range of the LSE/delta reads
-    const bool ragged = t * QT + QT > nq;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const float4 l4 = *reinterpret_cast<const float4*>(lse_s + gq * 8 + half * 4);
@@ -238,11 +251,18 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = 4 * gq + r;
-        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[r] * kLog2e));
-        if (ragged && t * QT + 8 * gq + 4 * half + r >= nq) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], c2, -lv[r] * kLog2e));
         sacc[v] = pv;
         dpacc[v] = pv * (dpacc[v] - dv4[r]);
       }
+    }
+    if (t * QT + QT > nq) {   // ragged last tile (uniform branch): no P, dS past the end
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (t * QT + 8 * (v >> 2) + 4 * half + (v & 3) >= nq) {
+          sacc[v] = 0.f;
+          dpacc[v] = 0.f;
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -302,7 +322,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 
 // ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
-template <int D, int NW, int KSUB, bool DENSE, typename GT>
+template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -317,6 +337,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];   // block_offset(r), r < S
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
@@ -347,6 +368,9 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
     for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: address of an empty stream
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
     __syncthreads();
     nkeys = kept * g.S;
   }
@@ -378,28 +402,33 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int CPR = D / 8;
   const int lrow0 = w * (KT / NW) + lane / CPR;
   const int lcp = lane % CPR;
-  // addresses first, then the loads back to back (no branch join in between)
-  auto issue_tile = [&](int t, unsigned char* sb) {
-    int32_t off[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int p = min(t * KT + lrow0 + i * RPI, nkeys - 1);
-      int32_t x = p;
-      if constexpr (!DENSE) {
-        const uint32_t bi = fd_div(uint32_t(p), g.div_S);
-        x = cols[bi] + block_offset(g, uint32_t(p) - bi * uint32_t(g.S));
-      }
-      off[i] = row_offset(g, grp, x);
-    }
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  const int plast = max(nkeys - 1, 0);   // positions past the end repeat the last key
+  // element offsets of this lane's K/V rows of tile t (addresses first, loads back to back)
+  auto tile_offsets = [&](int t, int32_t (&o)[LPW]) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = lrow0 + i * RPI;
-      const int32_t o = off[i] + (lcp ^ swz<D>(r)) * 8;
-      const int dst = (w * (KT / NW) + i * RPI) * ROWB;
-      load_to_lds16(K + o, sb + dst);
-      load_to_lds16(V + o, sb + TILE + dst);
+      const int p = min(t * KT + r, plast);
+      int32_t x = p;
+      if constexpr (!DENSE) {
+        const uint32_t bi = fd_div(uint32_t(p), g.div_S);
+        const uint32_t rr = uint32_t(p) - bi * uint32_t(g.S);
+        x = cols[bi] + (TAB ? offtab[rr] : block_offset(g, rr));
+      }
+      o[i] = gbase + x * hstride + (lcp ^ swz<D>(r)) * 8;
     }
   };
+  auto issue_offsets = [&](const int32_t (&o)[LPW], unsigned char* sb) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int dst = (w * (KT / NW) + i * RPI) * ROWB;
+      load_to_lds16(K + o[i], sb + dst);
+      load_to_lds16(V + o[i], sb + TILE + dst);
+    }
+  };
+  int32_t noff[LPW];   // addresses of the next tile, computed one step ahead
 
   const float c2 = a.scale_log2;
   const int grp16 = lane >> 4, sl = lane & 15;
@@ -408,39 +437,76 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
     unsigned char* const cur = ST ? stage1 : stage0;
     unsigned char* const nxt = ST ? stage0 : stage1;
-    if (t + 1 < ntiles) issue_tile(t + 1, nxt);
+    if (t + 1 < ntiles) {
+      issue_offsets(noff, nxt);
+      tile_offsets(t + 2, noff);
+    }
     if (wave_busy) {
     const unsigned char* kb = cur;
     const unsigned char* vb = cur + TILE;
+    // While direct-to-LDS loads are in flight the compiler waits for every outstanding LDS
+    // read at the first use of any of them, so reads are issued in batches: the K and V
+    // fragments of half the d-steps, their products, the other half, and the K^T reads of
+    // dQ right after.
     f32x16 sacc[KSUB], dpacc[KSUB];
 #pragma unroll
-    for (int kk = 0; kk < KSUB; ++kk) {
+    for (int kk = 0; kk < KSUB; ++kk)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         sacc[kk][v] = 0.f;
         dpacc[kk][v] = 0.f;
       }
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int o = tile_off<D>(kk * 32 + l32, 2 * s + half);
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + o));
-        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + o));
-        sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc[kk], 0, 0, 0);
-        dpacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[s], dpacc[kk], 0, 0, 0);
+    for (int hb = 0; hb < 2; ++hb) {
+      constexpr int HS = D / 32;   // d-steps per batch
+      bf16x8 ka[KSUB][HS], va[KSUB][HS];
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+        for (int j = 0; j < HS; ++j) {
+          const int o = tile_off<D>(kk * 32 + l32, 2 * (hb * HS + j) + half);
+          ka[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + o));
+          va[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(vb + o));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+        for (int j = 0; j < HS; ++j) {
+          sacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][j], qf[hb * HS + j],
+                                                             sacc[kk], 0, 0, 0);
+          dpacc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][j], df[hb * HS + j],
+                                                              dpacc[kk], 0, 0, 0);
+        }
+    }
+    bf16x8 kt[2 * KSUB][D / 32];   // K^T fragments of dQ^T += K^T dS^T (transposing reads)
+#pragma unroll
+    for (int ks = 0; ks < 2 * KSUB; ++ks) {
+      const int key0 = ks * 16 + 4 * half + (sl >> 2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
+        const int bo = (sl & 1) * 8;
+        const u32x2 lo = lds_read_tr16(kb + tile_off<D>(key0, c) + bo);
+        const u32x2 hi = lds_read_tr16(kb + tile_off<D>(key0 + 8, c) + bo);
+        kt[ks][dt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
     }
-    const bool ragged = t * KT + KT > nkeys;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kk][v], c2, -lse2));
-        if (ragged) {
-          const int key = t * KT + kk * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key >= nkeys) pv = 0.f;
-        }
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kk][v], c2, -lse2));
         dpacc[kk][v] = pv * (dpacc[kk][v] - dl);
       }
+    if (t * KT + KT > nkeys) {   // ragged last tile (uniform branch): no dS past the end
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (t * KT + kk * 32 + 8 * (v >> 2) + 4 * half + (v & 3) >= nkeys) dpacc[kk][v] = 0.f;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
       const int kk = ks >> 1, g0 = (ks & 1) * 8;
@@ -449,16 +515,9 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
       for (int e = 0; e < 4; ++e)
         sw[e] = pack_bf16x2(dpacc[kk][g0 + 2 * e], dpacc[kk][g0 + 2 * e + 1]);
       const bf16x8 sbf = as_bf16x8(sw);
-      const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
-        const int bo = (sl & 1) * 8;
-        const u32x2 lo = lds_read_tr16(kb + tile_off<D>(key0, c) + bo);
-        const u32x2 hi = lds_read_tr16(kb + tile_off<D>(key0 + 8, c) + bo);
-        dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), sbf, dqacc[dt], 0, 0, 0);
-      }
+      for (int dt = 0; dt < D / 32; ++dt)
+        dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks][dt], sbf, dqacc[dt], 0, 0, 0);
     }
     }
     wait_lds_loads();
@@ -467,7 +526,9 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (ntiles > 0) issue_tile(0, stage0);
+  tile_offsets(0, noff);
+  if (ntiles > 0) issue_offsets(noff, stage0);
+  tile_offsets(1, noff);
   wait_lds_loads();
   __syncthreads();
   int t = 0;
@@ -670,8 +731,11 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
-  attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, GT>
-      <<<xcd_grid(g.B * g.Hh, rows * a.tiles), NWK * 64, 0, s>>>(a);
+  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, !DENSE, GT><<<grid, NWK * 64, 0, s>>>(a);
+  else
+    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, false, GT><<<grid, NWK * 64, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT>
@@ -681,8 +745,11 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;
-  attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, GT>
-      <<<xcd_grid(g.B * g.Hh, rows * a.tiles), 256, 0, s>>>(a);
+  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT><<<grid, 256, 0, s>>>(a);
+  else
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT><<<grid, 256, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>
