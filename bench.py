@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every bf16 workload, layer and tau (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter scale)")
     return ap.parse_args()
@@ -87,46 +89,59 @@ def cpu_baseline(inp, cfg, spec, tau, min_seconds=10.0, max_heads=4):
                       f"algorithmic", "seconds": dt}
 
 
-def recorded_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
-    there is none for this workload or the kernel's source changed since it was taken."""
+def _kernel_source_hash(kernel):
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    src = {"attn_fwd_bf16_kernel": "attn_fwd.hip", "attn_bwd_dkdv_bf16_kernel": "attn_bwd.hip",
+    src = {"attn_fwd_bf16_kernel": "attn_fwd.hip", "attn_fwd16_bf16_kernel": "attn_fwd.hip",
+           "attn_bwd_dkdv_bf16_kernel": "attn_bwd.hip",
            "attn_bwd_dq_bf16_kernel": "attn_bwd.hip"}[kernel]
     h = hashlib.sha256()
     for fn in (src, "attn_common.h", "device_common.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_layer_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_counters(kernel, workload):
+    """Per-launch counter record of `kernel` (sparse instance) from the committed summary,
+    or None when there is none for this workload or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    want = _kernel_source_hash(kernel)
     for entry in rec["kernels"].values():   # the counter runs launch no dense baseline
-        if entry["kernel"] == kernel and entry["source_sha"] == h.hexdigest()[:16]:
-            return entry["traffic_bytes"]
+        if entry["kernel"] == kernel and entry["source_sha"] == want:
+            return entry
     return None
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the layer "
-              f"would shard over heads, see the design notes).", file=sys.stderr)
-        sys.exit(2)
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel`, copy-calibrated FETCH_SIZE + WRITE_SIZE, or None."""
+    entry = recorded_counters(kernel, workload)
+    return None if entry is None else entry["traffic_bytes"]
 
+
+def fwd_kernel_name(qlim, head_dim, bf16):
+    """The forward kernel the library launches: 48 queries per wave (16x16x32 MFMA) at
+    d = 128 when 192-query tiles pad no more than 128-query ones."""
+    if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= -(-qlim // 128) * 128:
+        return "attn_fwd16_bf16_kernel"
+    return "attn_fwd_bf16_kernel"
+
+
+def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample):
+    """Time the hot path of one layer of a workload; returns a dict of measurements."""
     import torch
     from synthetic import CONFIGS, make_layer_inputs
     import block_sparse_attention_layer_amd as vm
 
-    cfg = CONFIGS[args.workload]
-    spec = cfg["layers"][args.layer]
-    tau = args.tau if args.tau is not None else (0.25 if 0.25 in cfg["taus"] else cfg["taus"][0])
+    cfg = CONFIGS[workload]
+    spec = cfg["layers"][layer]
+    if tau is None:
+        tau = 0.25 if 0.25 in cfg["taus"] else cfg["taus"][0]
     dev = torch.device("cuda:0")
-    inp = make_layer_inputs(args.workload, args.layer, backward=True)
+    inp = make_layer_inputs(workload, layer, backward=True)
     dtype = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     p = vm.Problem(cfg["batch"], cfg["heads"], cfg["head_dim"], cfg["T"], cfg["H"], cfg["W"],
                    spec.layer_idx, tuple(spec.block), dtype, dtype)
@@ -134,7 +149,6 @@ def main():
     nb = vm.vmoba_num_blocks(p)
     S = p.L // nb
     d = p.head_dim
-
     names = ["pool", "select", "fwd", "delta", "dkdv", "dq"]
 
     def step(ev=None):
@@ -150,63 +164,116 @@ def main():
         mark(3)
         delta = vm.vmoba_sparse_attn_bwd_delta(p, o, do)
         mark(4)
-        dk, dv = vm.vmoba_sparse_attn_bwd_dkdv(p, q, k, v, lse, delta, do, sel.col_ptr,
-                                               sel.row_idx)
+        vm.vmoba_sparse_attn_bwd_dkdv(p, q, k, v, lse, delta, do, sel.col_ptr, sel.row_idx)
         mark(5)
-        dq = vm.vmoba_sparse_attn_bwd_dq(p, q, k, v, lse, delta, do, sel.row_ptr,
-                                         sel.col_idx)
+        vm.vmoba_sparse_attn_bwd_dq(p, q, k, v, lse, delta, do, sel.row_ptr, sel.col_idx)
         mark(6)
         return sel
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         sel = step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         sel = step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
                 for j, n in enumerate(names)}
 
     nnz = float(sel.head_stats[:, 1].double().sum().item())
     pairs = nnz * S * S
-    density = nnz / (p.groups * nb * nb)
     fl = {"fwd": 4.0 * d * pairs, "dkdv": 6.0 * d * pairs, "dq": 2.0 * d * pairs}
     executed = {"fwd": 4.0 * d * pairs, "dkdv": 8.0 * d * pairs, "dq": 6.0 * d * pairs}
-    total_flops = 12.0 * d * pairs
-    value = total_flops / (ms_step * 1e-3) / 1e12
-
-    attn = ["fwd", "dkdv", "dq"]
-    dom = max(attn, key=lambda n: stage_ms[n])
-    achieved = fl[dom] / (stage_ms[dom] * 1e-3) / 1e12
     esz = 2 if dtype == torch.bfloat16 else 4
     pool_bytes = 2.0 * p.L * p.groups * d * esz + 2.0 * p.groups * nb * d * 4
     select_bytes = 2.0 * p.groups * nb * d * 4 + 6.0 * p.groups * nb * nb * 4
-    kernel_names = {"fwd": "attn_fwd_bf16_kernel", "dkdv": "attn_bwd_dkdv_bf16_kernel",
-                    "dq": "attn_bwd_dq_bf16_kernel"}
+    kernel_names = {"fwd": fwd_kernel_name(S, d, dtype == torch.bfloat16),
+                    "dkdv": "attn_bwd_dkdv_bf16_kernel", "dq": "attn_bwd_dq_bf16_kernel"}
 
     dense = None
-    if not args.no_dense:
+    if dense_reps > 0:
         o_d, lse_d = vm.vmoba_dense_attn_fwd(p, q, k, v)
         vm.vmoba_dense_attn_bwd(p, q, k, v, o_d, lse_d, do)
         torch.cuda.synchronize()
-        reps = 2
         t1 = time.perf_counter()
-        for _ in range(reps):
+        for _ in range(dense_reps):
             o_d, lse_d = vm.vmoba_dense_attn_fwd(p, q, k, v)
             vm.vmoba_dense_attn_bwd(p, q, k, v, o_d, lse_d, do)
         torch.cuda.synchronize()
-        dense = (time.perf_counter() - t1) * 1e3 / reps
+        dense = (time.perf_counter() - t1) * 1e3 / dense_reps
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_sample:
         cpu = cpu_baseline(inp, cfg, spec, tau)
         cpu.pop("seconds")
+    return dict(cfg=cfg, spec=spec, tau=tau, p=p, nb=nb, S=S, d=d, dtype=dtype,
+                ms_step=ms_step, stage_ms=stage_ms, pairs=pairs,
+                density=nnz / (p.groups * nb * nb), fl=fl, executed=executed,
+                pool_bytes=pool_bytes, select_bytes=select_bytes, kernel_names=kernel_names,
+                dense=dense, cpu=cpu)
 
+
+def describe(workload, r):
+    p, spec = r["p"], r["spec"]
+    return (f"{workload}: layer_idx {spec.layer_idx} (l mod 3 = {spec.layer_idx % 3}), latent "
+            f"{p.T}x{p.H}x{p.W} = {p.L} tokens, {p.heads} heads x {r['d']}, blocks "
+            f"{tuple(spec.block)} ({r['nb']} blocks of {r['S']}), tau {r['tau']}, "
+            f"pool+select+sparse fwd+bwd")
+
+
+def summary(r):
+    """Per-stage figures shared by the contract line and the sweep lines."""
+    sm, fl, pairs, d = r["stage_ms"], r["fl"], r["pairs"], r["d"]
+    attn = ["fwd", "dkdv", "dq"]
+    ms = r["ms_step"]
+    return {
+        "stages_ms": {n: round(sm[n], 4) for n in sm},
+        "attn_ms": round(sum(sm[n] for n in ("fwd", "delta", "dkdv", "dq")), 4),
+        "stage_tflops": {n: round(fl[n] / (sm[n] * 1e-3) / 1e12, 2) for n in attn},
+        "stage_frac_bf16_peak": {n: round(fl[n] / (sm[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                                 for n in attn},
+        "tflops_fa_convention": round((4.0 + 10.0) * d * pairs / (ms * 1e-3) / 1e12, 2),
+        "pool_gbs": round(r["pool_bytes"] / (sm["pool"] * 1e-3) / 1e9, 1),
+        "pool_frac_hbm": round(r["pool_bytes"] / (sm["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "select_gbs": round(r["select_bytes"] / (sm["select"] * 1e-3) / 1e9, 1),
+        "select_frac_hbm": round(r["select_bytes"] / (sm["select"] * 1e-3) / 1e9 /
+                                 PEAK_HBM_GBS, 5),
+        "kept_pair_density": round(r["density"], 5),
+        "selected_token_pairs": pairs,
+        "dense_ms_per_step": None if r["dense"] is None else round(r["dense"], 3),
+        "speedup_vs_dense": None if r["dense"] is None else round(r["dense"] / ms, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the layer "
+              f"would shard over heads, see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
+
+    r = run_config(args.workload, args.layer, args.tau, args.steps, args.warmup,
+                   0 if args.no_dense else 2, not args.no_cpu_baseline)
+    ms_step, stage_ms, fl = r["ms_step"], r["stage_ms"], r["fl"]
+    value = 12.0 * r["d"] * r["pairs"] / (ms_step * 1e-3) / 1e12
+    dom = max(["fwd", "dkdv", "dq"], key=lambda n: stage_ms[n])
+    kname = r["kernel_names"][dom]
+    achieved = fl[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    counters = recorded_counters(kname, args.workload)
+    mfma_util = None
+    if counters is not None and counters.get("mfma_mops") is not None:
+        # executed MFMA work (512 flops per MOP) over the live launch time at peak
+        mfma_util = counters["mfma_mops"] * 512.0 / (stage_ms[dom] * 1e-3) / (
+            PEAK_BF16_TFLOPS * 1e12)
     line = {
         "metric": "VMoBA attn fwd+bwd ms/layer & TFLOP/s (% bf16 MFMA peak) at 55K tokens",
         "value": round(value, 2),
@@ -218,39 +285,43 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dtype == torch.bfloat16 else "fp32",
+        "dtype": "bf16" if str(r["dtype"]) == "torch.bfloat16" else "fp32",
         "data": "synthetic",
-        "config": {
-            "workload": f"{args.workload}: layer_idx {spec.layer_idx} (l mod 3 = "
-                        f"{spec.layer_idx % 3}), latent {p.T}x{p.H}x{p.W} = {p.L} tokens, "
-                        f"{p.heads} heads x {d}, blocks {tuple(spec.block)} ({nb} blocks of "
-                        f"{S}), tau {tau}, pool+select+sparse fwd+bwd",
-            "global_batch": p.batch, "seq_len": p.L, "parallelism": "none (1 GPU)"},
+        "config": {"workload": describe(args.workload, r), "global_batch": r["p"].batch,
+                   "seq_len": r["p"].L, "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": kernel_names[dom], "bound": "mfma",
+            "kernel": kname, "bound": "mfma",
             "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_traffic(kernel_names[dom], args.workload),
+            "traffic": None if counters is None else counters["traffic_bytes"],
             "traffic_unit": "HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, copy-calibrated)",
             "avg_ms": round(stage_ms[dom], 4),
             "algorithmic_flops_per_launch": fl[dom],
-            "executed_flops_per_launch": executed[dom]},
-        "cpu_baseline": cpu,
-        "stages_ms": {n: round(stage_ms[n], 4) for n in names},
-        "stage_tflops": {n: round(fl[n] / (stage_ms[n] * 1e-3) / 1e12, 2) for n in attn},
-        "stage_frac_bf16_peak": {n: round(fl[n] / (stage_ms[n] * 1e-3) / 1e12 /
-                                          PEAK_BF16_TFLOPS, 4) for n in attn},
-        "pool_gbs": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9, 1),
-        "pool_frac_hbm": round(pool_bytes / (stage_ms["pool"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "select_gbs": round(select_bytes / (stage_ms["select"] * 1e-3) / 1e9, 1),
-        "select_frac_hbm": round(select_bytes / (stage_ms["select"] * 1e-3) / 1e9 /
-                                 PEAK_HBM_GBS, 5),
-        "kept_pair_density": round(density, 5),
-        "selected_token_pairs": pairs,
-        "dense_ms_per_step": None if dense is None else round(dense, 3),
-        "speedup_vs_dense": None if dense is None else round(dense / ms_step, 3),
+            "executed_flops_per_launch": r["executed"][dom],
+            "mfma_util_counter": None if mfma_util is None else round(mfma_util, 4)},
+        "cpu_baseline": r["cpu"],
     }
+    line.update(summary(r))
     print(json.dumps(line), flush=True)
+
+
+def sweep(args):
+    """One JSON line per workload layer and tau (the per-config report; not the contract
+    line).  Fewer steps, no CPU sample."""
+    from synthetic import CONFIGS, CONFIG_ORDER
+    for name in CONFIG_ORDER:
+        cfg = CONFIGS[name]
+        if cfg["dtype"] != "bf16":
+            continue
+        for layer in range(len(cfg["layers"])):
+            for tau in cfg["taus"]:
+                r = run_config(name, layer, tau, args.steps, args.warmup,
+                               0 if args.no_dense else 1, False)
+                line = {"workload": describe(name, r), "ms_per_step": round(r["ms_step"], 4),
+                        "tflops": round(12.0 * r["d"] * r["pairs"] / (r["ms_step"] * 1e-3) /
+                                        1e12, 2)}
+                line.update(summary(r))
+                print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
