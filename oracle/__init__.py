@@ -24,7 +24,9 @@ that takes it.  Modules:
 * :mod:`oracle.partition` — mode ``l mod 3`` and the block membership table.
 * :mod:`oracle.pooling` — block means of Q and K.
 * :mod:`oracle.selection` — block scores, per-head softmax normalisation and
-  the cumulative-mass threshold with the forced diagonal.
+  the cumulative-mass threshold with the forced diagonal; the ablation's other
+  strategies (top-k + global, threshold + local, top-k + local; paperlayer §4.4,
+  Table 3).
 * :mod:`oracle.attention` — masked softmax attention forward and backward
   (literal dense form, block-sparse form and sampled rows).
 
@@ -40,7 +42,8 @@ from .partition import (
 from .pooling import block_means
 from .selection import (
     block_scores, normalise_per_head, threshold_select, select_all_heads,
-    mask_to_csr, mask_to_csc,
+    mask_to_csr, mask_to_csc, topk_select, normalise_per_row, local_select,
+    SELECTION_MODES,
 )
 from .attention import (
     dense_masked_attention_fwd, dense_masked_attention_bwd, token_mask,
@@ -53,7 +56,8 @@ __all__ = [
     "MODE_1D", "MODE_2D", "MODE_3D", "partition_mode", "check_partition",
     "block_members", "block_of_token", "num_blocks", "block_means",
     "block_scores", "normalise_per_head", "threshold_select",
-    "select_all_heads", "mask_to_csr", "mask_to_csc",
+    "select_all_heads", "mask_to_csr", "mask_to_csc", "topk_select",
+    "normalise_per_row", "local_select", "SELECTION_MODES",
     "dense_masked_attention_fwd", "dense_masked_attention_bwd", "token_mask",
     "sparse_attention_fwd", "sparse_attention_bwd", "sampled_query_rows",
     "sampled_key_block_grads", "oracle_layer",

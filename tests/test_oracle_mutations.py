@@ -92,3 +92,34 @@ def test_block_mask_transposed_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "sparse_attention_fwd",
                         lambda q, k, v, mem, bm: orig(q, k, v, mem, np.swapaxes(bm, -1, -2)))
     assert _fails(t_att.test_block_sparse_matches_masked_sdpa_and_literal_form, 0, 0.3)
+
+
+import test_oracle_selection_modes as t_modes
+
+
+def test_modes_pins_pass_unmutated():
+    assert not _fails(t_modes.test_golden_local_and_topk_examples)
+    assert not _fails(t_modes.test_row_normalisation_is_row_softmax)
+
+
+def test_local_pool_normalised_over_the_head_is_caught(monkeypatch):
+    # planted slip: the local rule fed head-normalised scores (the global pool's shares)
+    monkeypatch.setattr(oracle, "normalise_per_row",
+                        lambda s: sel.normalise_per_head(np.asarray(s, float)[None, None])[0, 0]
+                        if np.ndim(s) == 2 else sel.normalise_per_head(s))
+    assert _fails(t_modes.test_golden_local_and_topk_examples)
+
+
+def test_topk_off_by_one_is_caught(monkeypatch):
+    orig = sel.topk_select
+    monkeypatch.setattr(oracle, "topk_select", lambda shat, k: orig(shat, k + 1))
+    assert _fails(t_modes.test_topk_global_keeps_a_dominant_set_of_exactly_k, 0)
+
+
+def test_local_strict_inequality_is_caught(monkeypatch):
+    orig = sel.local_select
+
+    def strict(shat_rows, tau=None, k=None):
+        return orig(shat_rows, tau=None if tau is None else np.nextafter(tau, 2.0), k=k)
+    monkeypatch.setattr(oracle, "local_select", strict)
+    assert _fails(t_modes.test_golden_local_and_topk_examples)
