@@ -36,6 +36,10 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--select-mode", default="threshold_global",
+                    choices=["threshold_global", "topk_global", "threshold_local", "topk_local"],
+                    help="selection strategy (the method's is threshold_global)")
+    ap.add_argument("--topk", type=int, default=None, help="k of the top-k strategies")
     ap.add_argument("--sweep", action="store_true",
                     help="time every bf16 workload, layer and tau (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -59,7 +63,8 @@ def calibrate_copy():
                       "launches": 3}), flush=True)
 
 
-def cpu_baseline(inp, cfg, spec, tau, min_seconds=10.0, max_heads=4):
+def cpu_baseline(inp, cfg, spec, tau, min_seconds=10.0, max_heads=4, mode="threshold_global",
+                 topk=None):
     """The fp64 oracle on the host cores, on whole heads of the same layer: head 0, then
     further heads while less than `min_seconds` have passed (at most `max_heads`)."""
     import oracle
@@ -77,7 +82,7 @@ def cpu_baseline(inp, cfg, spec, tau, min_seconds=10.0, max_heads=4):
         q, k, v, do = (inp[x][:, :, h].float().numpy() for x in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
         qp, kp = oracle.block_means(q, mem), oracle.block_means(k, mem)
-        mask, _, _ = oracle.select_all_heads(qp, kp, tau)
+        mask, _, _ = oracle.select_all_heads(qp, kp, tau, mode=mode, k=topk)
         o, lse = oracle.sparse_attention_fwd(q, k, v, mem, mask)
         oracle.sparse_attention_bwd(q, k, v, o, lse, do, mem, mask)
         dt += time.perf_counter() - t0
@@ -130,8 +135,10 @@ def fwd_kernel_name(qlim, head_dim, bf16):
     return "attn_fwd_bf16_kernel"
 
 
-def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample):
-    """Time the hot path of one layer of a workload; returns a dict of measurements."""
+def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
+               mode="threshold_global", topk=None):
+    """Time the hot path of one layer of a workload; returns a dict of measurements.
+    mode / topk choose the selection strategy (threshold_global, the method's, by default)."""
     import torch
     from synthetic import CONFIGS, make_layer_inputs
     import block_sparse_attention_layer_amd as vm
@@ -158,7 +165,7 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample):
         mark(0)
         qp, kp = vm.vmoba_partition_pool(p, q, k)
         mark(1)
-        sel = vm.vmoba_select(p, qp, kp, tau)
+        sel = vm.vmoba_select(p, qp, kp, tau, mode=mode, k=topk)
         mark(2)
         o, lse = vm.vmoba_sparse_attn_fwd(p, q, k, v, sel.row_ptr, sel.col_idx)
         mark(3)
@@ -207,9 +214,10 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample):
 
     cpu = None
     if cpu_sample:
-        cpu = cpu_baseline(inp, cfg, spec, tau)
+        cpu = cpu_baseline(inp, cfg, spec, tau, mode=mode, topk=topk)
         cpu.pop("seconds")
-    return dict(cfg=cfg, spec=spec, tau=tau, p=p, nb=nb, S=S, d=d, dtype=dtype,
+    return dict(cfg=cfg, spec=spec, tau=tau, mode=mode, topk=topk, p=p, nb=nb, S=S, d=d,
+                dtype=dtype,
                 ms_step=ms_step, stage_ms=stage_ms, pairs=pairs,
                 density=nnz / (p.groups * nb * nb), fl=fl, executed=executed,
                 pool_bytes=pool_bytes, select_bytes=select_bytes, kernel_names=kernel_names,
@@ -218,9 +226,11 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample):
 
 def describe(workload, r):
     p, spec = r["p"], r["spec"]
+    sel = ("" if r.get("mode", "threshold_global") == "threshold_global"
+           else f", selection {r['mode']} k {r['topk']}")
     return (f"{workload}: layer_idx {spec.layer_idx} (l mod 3 = {spec.layer_idx % 3}), latent "
             f"{p.T}x{p.H}x{p.W} = {p.L} tokens, {p.heads} heads x {r['d']}, blocks "
-            f"{tuple(spec.block)} ({r['nb']} blocks of {r['S']}), tau {r['tau']}, "
+            f"{tuple(spec.block)} ({r['nb']} blocks of {r['S']}), tau {r['tau']}{sel}, "
             f"pool+select+sparse fwd+bwd")
 
 
@@ -262,7 +272,8 @@ def main():
         return
 
     r = run_config(args.workload, args.layer, args.tau, args.steps, args.warmup,
-                   0 if args.no_dense else 2, not args.no_cpu_baseline)
+                   0 if args.no_dense else 2, not args.no_cpu_baseline,
+                   args.select_mode, args.topk)
     ms_step, stage_ms, fl = r["ms_step"], r["stage_ms"], r["fl"]
     value = 12.0 * r["d"] * r["pairs"] / (ms_step * 1e-3) / 1e12
     dom = max(["fwd", "dkdv", "dq"], key=lambda n: stage_ms[n])

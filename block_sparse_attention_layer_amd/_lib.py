@@ -40,6 +40,9 @@ _SIG = {
     "vmoba_partition_pool": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, _P, _P, _P]),
     "vmoba_select": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, ctypes.c_float, _P, _P,
                                     _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "vmoba_select_mode": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, ctypes.c_int,
+                                         ctypes.c_float, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                         _P, _P, ctypes.c_size_t, _P]),
     "vmoba_sparse_attn_fwd": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, _P, _P, _P,
                                              _P, _P, _P, ctypes.c_size_t, _P]),
     "vmoba_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 14 +

@@ -128,7 +128,17 @@ class Selection:
     norm_scores: Optional[torch.Tensor] = None  # fp32 [G, N_b, N_b]
 
 
-def vmoba_select(p: Problem, q_pool, k_pool, tau: float, want_scores=False) -> Selection:
+SELECTION_MODES = {"threshold_global": 0, "topk_global": 1, "threshold_local": 2,
+                   "topk_local": 3}
+
+
+def vmoba_select(p: Problem, q_pool, k_pool, tau: float = None, want_scores=False,
+                 mode: str = "threshold_global", k: int = None) -> Selection:
+    """Block selection.  mode "threshold_global" (the default, tau) is vmoba_select; the
+    other SELECTION_MODES go through vmoba_select_mode (tau for threshold_local, k for the
+    top-k modes)."""
+    if mode not in SELECTION_MODES:
+        raise ValueError(f"unknown selection mode {mode!r}")
     dev = q_pool.device
     nb = vmoba_num_blocks(p)
     G = p.groups
@@ -144,10 +154,21 @@ def vmoba_select(p: Problem, q_pool, k_pool, tau: float, want_scores=False) -> S
                      if want_scores else None))
     ws, n = _workspace(p, "select", dev)
     s = p.c_struct()
-    check(lib().vmoba_select(ctypes.byref(s), _ptr(q_pool), _ptr(k_pool), ctypes.c_float(tau),
-                             _ptr(sel.row_ptr), _ptr(sel.col_idx), _ptr(sel.col_ptr),
-                             _ptr(sel.row_idx), _ptr(sel.head_stats), _ptr(sel.norm_scores),
-                             _ptr(ws), n, _stream(dev)), "vmoba_select")
+    if mode == "threshold_global":
+        check(lib().vmoba_select(ctypes.byref(s), _ptr(q_pool), _ptr(k_pool),
+                                 ctypes.c_float(tau), _ptr(sel.row_ptr), _ptr(sel.col_idx),
+                                 _ptr(sel.col_ptr), _ptr(sel.row_idx), _ptr(sel.head_stats),
+                                 _ptr(sel.norm_scores), _ptr(ws), n, _stream(dev)),
+              "vmoba_select")
+    else:
+        check(lib().vmoba_select_mode(ctypes.byref(s), _ptr(q_pool), _ptr(k_pool),
+                                      SELECTION_MODES[mode],
+                                      ctypes.c_float(0.0 if tau is None else tau),
+                                      ctypes.c_int32(0 if k is None else int(k)),
+                                      _ptr(sel.row_ptr), _ptr(sel.col_idx), _ptr(sel.col_ptr),
+                                      _ptr(sel.row_idx), _ptr(sel.head_stats),
+                                      _ptr(sel.norm_scores), _ptr(ws), n, _stream(dev)),
+              "vmoba_select_mode")
     return sel
 
 

@@ -48,8 +48,29 @@ int vmoba_select(const vmoba_problem* p, const float* q_pool, const float* k_poo
   if (!q_pool || !k_pool || !row_ptr || !col_idx || !col_ptr || !row_idx || !head_stats)
     return VMOBA_ERR_NULL;
   if ((st = check_ws(p, VMOBA_OP_SELECT, ws, ws_bytes))) return st;
-  return launch_select(make_geom(p), q_pool, k_pool, tau, row_ptr, col_idx, col_ptr,
-                       row_idx, head_stats, norm_scores, ws, stream);
+  return launch_select(make_geom(p), q_pool, k_pool, VMOBA_SEL_THRESHOLD_GLOBAL, tau, 0,
+                       row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores, ws,
+                       stream);
+}
+
+int vmoba_select_mode(const vmoba_problem* p, const float* q_pool, const float* k_pool,
+                      int mode, float tau, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
+                      int32_t* col_ptr, int32_t* row_idx, float* head_stats,
+                      float* norm_scores, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_blocks(p))) return st;
+  const bool thr = mode == VMOBA_SEL_THRESHOLD_GLOBAL || mode == VMOBA_SEL_THRESHOLD_LOCAL;
+  const bool tk = mode == VMOBA_SEL_TOPK_GLOBAL || mode == VMOBA_SEL_TOPK_LOCAL;
+  if (!thr && !tk) return VMOBA_ERR_SELECT;
+  if (thr && (!(tau > 0.0f) || !(tau <= 1.0f) || !isfinite(tau))) return VMOBA_ERR_TAU;
+  if (tk && topk < 1) return VMOBA_ERR_SELECT;
+  if (!q_pool || !k_pool || !row_ptr || !col_idx || !col_ptr || !row_idx || !head_stats)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_SELECT, ws, ws_bytes))) return st;
+  return launch_select(make_geom(p), q_pool, k_pool, mode, thr ? tau : 0.0f,
+                       tk ? topk : 0, row_ptr, col_idx, col_ptr, row_idx, head_stats,
+                       norm_scores, ws, stream);
 }
 
 int vmoba_sparse_attn_fwd(const vmoba_problem* p, const void* q, const void* k,

@@ -14,6 +14,9 @@ namespace vmoba {
 // kernel keeps the N_b x N_b pair bitmap of one head in LDS (128 KiB at 1024 blocks).
 constexpr int kMaxBlocks = 1024;
 
+// Workspace buffers start on 256-byte boundaries.
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 int validate_problem(const vmoba_problem* p);
 Geom make_geom(const vmoba_problem* p);
 int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes);
@@ -22,8 +25,9 @@ int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes);
 int launch_pool(const Geom& g, const void* q, const void* k, float* q_pool,
                 float* k_pool, void* stream);
 
-int launch_select(const Geom& g, const float* q_pool, const float* k_pool, float tau,
-                  int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
+// mode: vmoba_selection; tau for the threshold modes, topk for the top-k modes.
+int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int mode, float tau,
+                  int topk, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
                   int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
                   void* stream);
 

@@ -17,6 +17,16 @@
 //   3. Compaction in linear order marks the prefix plus the diagonal in an LDS bitmap
 //      (wave ballots, one 64-bit word per wave), then row and column counts, an
 //      exclusive scan and an ascending walk per row / column emit CSR and CSC.
+//   With TOPK the same walk counts pairs instead of mass: the cutoff is the key of the
+//   k-th pair (top-k + global, one of the strategies of the ablation, paperlayer §4.4).
+//
+// Local strategies (threshold + local, top-k + local): every query block's row of N_b
+// scores is its own pool, normalised by a softmax over the row.  select_local_kernel
+// gives each row one wave; a pair is kept iff the fixed-point mass (threshold) or the
+// number (top-k) of the row's pairs that precede it in the order (higher score, or the
+// same score at a lower key index) is below the target.  Each lane counts that for its
+// pairs against the whole row staged in LDS.  The rows go to a bitmap, and
+// emit_lists_kernel turns the bitmap into CSR and CSC as above.
 #include <math.h>
 
 #include "device_common.h"
@@ -162,8 +172,9 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   return off + x - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void threshold_select_kernel(
-    int Nb, float tau, const float* __restrict__ scores, int32_t* __restrict__ row_ptr,
+template <bool TOPK>
+__global__ __launch_bounds__(kSelThreads) void global_select_kernel(
+    int Nb, float tau, int topk, const float* __restrict__ scores, int32_t* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, int32_t* __restrict__ col_ptr,
     int32_t* __restrict__ row_idx, float* __restrict__ head_stats,
     float* __restrict__ norm_scores) {
@@ -184,9 +195,14 @@ __global__ __launch_bounds__(kSelThreads) void threshold_select_kernel(
   if (tid == 0) {
     sh.m = mx;
     sh.Z = z;
-    const double r = ceil(double(tau) * double(z));
-    sh.R = (unsigned long long)r;
-    sh.select_all = (tau >= 1.0f || sh.R > z) ? 1u : 0u;
+    if constexpr (TOPK) {
+      sh.R = (unsigned long long)topk;   // a count of pairs
+      sh.select_all = topk >= N ? 1u : 0u;
+    } else {
+      const double r = ceil(double(tau) * double(z));
+      sh.R = (unsigned long long)r;
+      sh.select_all = (tau >= 1.0f || sh.R > z) ? 1u : 0u;
+    }
     sh.prefix = 0;
     sh.above_cnt = 0;
     sh.above_mass = 0;
@@ -219,7 +235,8 @@ __global__ __launch_bounds__(kSelThreads) void threshold_select_kernel(
         uint32_t cnt = sh.above_cnt;
         int dg = 255;
         for (; dg >= 0; --dg) {
-          if (acc + sh.mass[dg] >= sh.R && sh.cnt[dg] > 0) break;
+          const bool reach = TOPK ? cnt + sh.cnt[dg] >= sh.R : acc + sh.mass[dg] >= sh.R;
+          if (reach && sh.cnt[dg] > 0) break;
           acc += sh.mass[dg];
           cnt += sh.cnt[dg];
         }
@@ -240,8 +257,8 @@ __global__ __launch_bounds__(kSelThreads) void threshold_select_kernel(
   if (tid == 0 && !sh.select_all) {
     // all tied pairs share one score, hence one fixed-point mass
     const unsigned long long e1 = sh.tie_mass / sh.tie_cnt;
-    const unsigned long long need = sh.R - sh.above_mass;
-    unsigned long long t = e1 ? (need + e1 - 1) / e1 : 1;
+    const unsigned long long need = sh.R - (TOPK ? sh.above_cnt : sh.above_mass);
+    unsigned long long t = TOPK ? need : (e1 ? (need + e1 - 1) / e1 : 1);
     if (t < 1) t = 1;
     if (t > sh.tie_cnt) t = sh.tie_cnt;
     sh.take_ties = uint32_t(t);
@@ -349,12 +366,224 @@ __global__ __launch_bounds__(kSelThreads) void threshold_select_kernel(
   }
 }
 
-int launch_select(const Geom& g, const float* q_pool, const float* k_pool, float tau,
-                  int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
+// One wave per query-block row; U = ceil(N_b / 64) pairs per lane.  rowstats[G][N_b][3] =
+// {prefix length, prefix mass fraction, smallest normalised score in the prefix}.
+template <bool TOPK, int U>
+__global__ __launch_bounds__(256) void select_local_kernel(
+    int Nb, float tau, int topk, const float* __restrict__ scores, uint32_t* __restrict__ bitmap,
+    float* __restrict__ rowstats, float* __restrict__ norm_scores) {
+  constexpr int WPB = 4;
+  __shared__ float vs[WPB][64 * U];
+  __shared__ unsigned long long es[WPB][64 * U];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int grp = blockIdx.y;
+  const int i = blockIdx.x * WPB + w;
+  if (i >= Nb) return;   // a whole wave; nothing below synchronises across waves
+  const float* srow = scores + (size_t(grp) * Nb + i) * Nb;
+
+  float v[U];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = lane + 64 * u;
+    v[u] = j < Nb ? srow[j] : -INFINITY;
+    mx = fmaxf(mx, v[u]);
+  }
+  mx = wave_max(mx);
+  unsigned long long e[U], z = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = lane + 64 * u;
+    e[u] = j < Nb ? fixed_mass(v[u], mx) : 0ull;
+    z += e[u];
+    vs[w][j] = v[u];
+    es[w][j] = e[u];
+  }
+  z = wave_sum_u64(z);
+  // the wave's own LDS writes become visible to its other lanes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  unsigned long long target;
+  bool all;
+  if constexpr (TOPK) {
+    target = (unsigned long long)topk;
+    all = topk >= Nb;
+  } else {
+    target = (unsigned long long)ceil(double(tau) * double(z));
+    all = tau >= 1.0f || target > z;
+  }
+  // mass (threshold) or count (top-k) of the row's pairs ahead of each of this lane's
+  unsigned long long before[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) before[u] = 0;
+  for (int jj = 0; jj < Nb; ++jj) {
+    const float vj = vs[w][jj];
+    const unsigned long long ej = TOPK ? 1ull : es[w][jj];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = lane + 64 * u;
+      if (vj > v[u] || (vj == v[u] && jj < j)) before[u] += ej;
+    }
+  }
+
+  const int W = (Nb + 31) / 32;
+  uint32_t* brow = bitmap + (size_t(grp) * Nb + i) * W;
+  const float inv_z = float(kMassUnit / double(z));
+  unsigned long long pmass = 0;
+  int pcnt = 0;
+  float vmin = INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = lane + 64 * u;
+    const bool in = j < Nb;
+    const bool pre = in && (all || before[u] < target);
+    const bool sel = pre || (in && j == i);
+    const unsigned long long bm = __ballot(sel);
+    if (lane == 0) {
+      if (2 * u < W) brow[2 * u] = uint32_t(bm);
+      if (2 * u + 1 < W) brow[2 * u + 1] = uint32_t(bm >> 32);
+    }
+    pcnt += __popcll(__ballot(pre));
+    if (pre) {
+      pmass += e[u];
+      vmin = fminf(vmin, float(double(e[u]) / double(z)));
+    }
+    if (norm_scores && in)
+      norm_scores[(size_t(grp) * Nb + i) * Nb + j] = expf(v[u] - mx) * inv_z;
+  }
+  pmass = wave_sum_u64(pmass);
+  vmin = -wave_max(-vmin);
+  if (lane == 0) {
+    float* rs = rowstats + (size_t(grp) * Nb + i) * 3;
+    rs[0] = float(pcnt);
+    rs[1] = float(double(pmass) / double(z));
+    rs[2] = pcnt ? vmin : 0.0f;
+  }
+}
+
+// CSR and CSC of one head group from a row-aligned pair bitmap (N_b rows of
+// ceil(N_b/32) words), plus head_stats = {sum of prefix lengths, nnz, mean prefix mass,
+// mean smallest prefix score} over the rows.
+__global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
+    int Nb, const uint32_t* __restrict__ bitmap, const float* __restrict__ rowstats,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+    int32_t* __restrict__ col_ptr, int32_t* __restrict__ row_idx,
+    float* __restrict__ head_stats) {
+  __shared__ SelShared sh;
+  extern __shared__ uint32_t bits[];
+  const int grp = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int W = (Nb + 31) / 32;
+  const uint32_t* src = bitmap + size_t(grp) * Nb * W;
+  for (int x = tid; x < Nb * W; x += kSelThreads) bits[x] = src[x];
+  __syncthreads();
+  auto bit = [&](int i, int j) { return (bits[i * W + (j >> 5)] >> (j & 31)) & 1u; };
+  for (int i = tid; i < Nb; i += kSelThreads) {
+    int rc = 0, cc = 0;
+    for (int x = 0; x < W; ++x) rc += __popc(bits[i * W + x]);
+    for (int r = 0; r < Nb; ++r) cc += bit(r, i);
+    sh.row_cnt[i] = rc;
+    sh.col_cnt[i] = cc;
+  }
+  __syncthreads();
+  int32_t* rp = row_ptr + size_t(grp) * (Nb + 1);
+  int32_t* cp = col_ptr + size_t(grp) * (Nb + 1);
+  float ks = 0.f, ms = 0.f, vsum = 0.f;
+  for (int i = tid; i < Nb; i += kSelThreads) {
+    const float* rs = rowstats + (size_t(grp) * Nb + i) * 3;
+    ks += rs[0];
+    ms += rs[1];
+    vsum += rs[2];
+  }
+  {
+    const int rc = tid < Nb ? sh.row_cnt[tid] : 0;
+    const int cc = tid < Nb ? sh.col_cnt[tid] : 0;
+    int rtot = 0, ctot = 0;
+    const int roff = block_excl_scan(rc, sh, &rtot);
+    const int coff = block_excl_scan(cc, sh, &ctot);
+    ks = wave_sum(ks);
+    ms = wave_sum(ms);
+    vsum = wave_sum(vsum);
+    __syncthreads();
+    if (tid < Nb) {
+      sh.row_cnt[tid] = roff;
+      sh.col_cnt[tid] = coff;
+      rp[tid] = roff;
+      cp[tid] = coff;
+    }
+    if ((tid & 63) == 0) {   // Nb <= kMaxBlocks = kSelThreads: sums of the first waves
+      sh.redf[tid >> 6] = ks;
+      sh.redi[tid >> 6] = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      rp[Nb] = rtot;
+      cp[Nb] = ctot;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) sh.redf[tid >> 6] = ms;
+    __syncthreads();
+    float mtot = 0.f;
+    if (tid == 0)
+      for (int x = 0; x < kSelWaves; ++x) mtot += sh.redf[x];
+    __syncthreads();
+    if ((tid & 63) == 0) sh.redf[tid >> 6] = vsum;
+    __syncthreads();
+    float vtot = 0.f;
+    if (tid == 0)
+      for (int x = 0; x < kSelWaves; ++x) vtot += sh.redf[x];
+    __syncthreads();
+    if ((tid & 63) == 0) sh.redf[tid >> 6] = ks;
+    __syncthreads();
+    if (tid == 0 && head_stats) {
+      float ktot = 0.f;
+      for (int x = 0; x < kSelWaves; ++x) ktot += sh.redf[x];
+      float* hs = head_stats + size_t(grp) * 4;
+      hs[0] = ktot;
+      hs[1] = float(rtot);
+      hs[2] = mtot / float(Nb);
+      hs[3] = vtot / float(Nb);
+    }
+  }
+  __syncthreads();
+  int32_t* ci = col_idx + size_t(grp) * Nb * Nb;
+  int32_t* ri = row_idx + size_t(grp) * Nb * Nb;
+  for (int i = tid; i < Nb; i += kSelThreads) {
+    int pr = sh.row_cnt[i], pc = sh.col_cnt[i];
+    for (int j = 0; j < Nb; ++j) {
+      if (bit(i, j)) ci[pr++] = j;
+      if (bit(j, i)) ri[pc++] = j;
+    }
+  }
+}
+
+template <bool TOPK>
+static int launch_local(const Geom& g, float tau, int topk, const float* scores,
+                        uint32_t* bitmap, float* rowstats, float* norm_scores, hipStream_t st) {
+  const int groups = g.B * g.Hh;
+  const dim3 grid((g.Nb + 3) / 4, groups);
+  const int U = (g.Nb + 63) / 64;
+  if (U <= 1)
+    select_local_kernel<TOPK, 1><<<grid, 256, 0, st>>>(g.Nb, tau, topk, scores, bitmap, rowstats, norm_scores);
+  else if (U <= 2)
+    select_local_kernel<TOPK, 2><<<grid, 256, 0, st>>>(g.Nb, tau, topk, scores, bitmap, rowstats, norm_scores);
+  else if (U <= 4)
+    select_local_kernel<TOPK, 4><<<grid, 256, 0, st>>>(g.Nb, tau, topk, scores, bitmap, rowstats, norm_scores);
+  else if (U <= 8)
+    select_local_kernel<TOPK, 8><<<grid, 256, 0, st>>>(g.Nb, tau, topk, scores, bitmap, rowstats, norm_scores);
+  else
+    select_local_kernel<TOPK, 16><<<grid, 256, 0, st>>>(g.Nb, tau, topk, scores, bitmap, rowstats, norm_scores);
+  return launch_status();
+}
+
+int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int mode, float tau,
+                  int topk, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
                   int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
                   void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int groups = g.B * g.Hh;
+  const size_t nb2 = size_t(g.Nb) * g.Nb;
   float* scores = static_cast<float*>(ws);
   const float scale = 1.0f / sqrtf(float(g.D));
   dim3 sgrid((g.Nb + 31) / 32, (g.Nb + 31) / 32, groups);
@@ -364,13 +593,38 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, float
     block_scores_kernel<64><<<sgrid, 64, 0, st>>>(g.Nb, q_pool, k_pool, scores, scale);
   int stt = launch_status();
   if (stt) return stt;
-  const size_t words = ((size_t(g.Nb) * g.Nb + 1023) / 1024) * 32;  // whole 1024-pair chunks
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(threshold_select_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          int(size_t(kMaxBlocks) * kMaxBlocks / 8)) != hipSuccess)
+  const int max_lds = int(size_t(kMaxBlocks) * kMaxBlocks / 8);
+  if (mode == VMOBA_SEL_THRESHOLD_GLOBAL || mode == VMOBA_SEL_TOPK_GLOBAL) {
+    const size_t words = ((nb2 + 1023) / 1024) * 32;  // whole 1024-pair chunks
+    const bool tk = mode == VMOBA_SEL_TOPK_GLOBAL;
+    const void* fn = tk ? reinterpret_cast<const void*>(global_select_kernel<true>)
+                        : reinterpret_cast<const void*>(global_select_kernel<false>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) !=
+        hipSuccess)
+      return VMOBA_ERR_HIP;
+    if (tk)
+      global_select_kernel<true><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
+          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+    else
+      global_select_kernel<false><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
+          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+    return launch_status();
+  }
+  // local strategies: bitmap and row statistics behind the scores in the workspace
+  const size_t W = (size_t(g.Nb) + 31) / 32;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + align256(groups * nb2 * sizeof(float)));
+  float* rowstats = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(bitmap) +
+                                             align256(groups * size_t(g.Nb) * W * 4));
+  stt = mode == VMOBA_SEL_TOPK_LOCAL
+            ? launch_local<true>(g, tau, topk, scores, bitmap, rowstats, norm_scores, st)
+            : launch_local<false>(g, tau, topk, scores, bitmap, rowstats, norm_scores, st);
+  if (stt) return stt;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
     return VMOBA_ERR_HIP;
-  threshold_select_kernel<<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
-      g.Nb, tau, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+  emit_lists_kernel<<<groups, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
+      g.Nb, bitmap, rowstats, row_ptr, col_idx, col_ptr, row_idx, head_stats);
   return launch_status();
 }
 

@@ -62,7 +62,6 @@ Geom make_geom(const vmoba_problem* p) {
   return g;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
   const Geom g = make_geom(p);
@@ -74,10 +73,15 @@ int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
     case VMOBA_OP_DENSE_FWD:
       *bytes = 0;
       return VMOBA_OK;
-    case VMOBA_OP_SELECT:
-      // raw block scores, fp32 per head group
-      *bytes = align256(groups * pool * sizeof(float));
+    case VMOBA_OP_SELECT: {
+      // raw block scores, fp32 per head group; the local modes add a row-aligned pair
+      // bitmap and three floats of statistics per row
+      const size_t words = (size_t(g.Nb) + 31) / 32;
+      *bytes = align256(groups * pool * sizeof(float)) +
+               align256(groups * size_t(g.Nb) * words * 4) +
+               align256(groups * size_t(g.Nb) * 3 * sizeof(float));
       return VMOBA_OK;
+    }
     case VMOBA_OP_SPARSE_BWD:
     case VMOBA_OP_DENSE_BWD:
       // delta = rowsum(dO * O), fp32 [B][Hh][L]
@@ -107,6 +111,7 @@ const char* vmoba_status_string(int status) {
     case VMOBA_ERR_OVERFLOW: return "problem too large for 32-bit indexing";
     case VMOBA_ERR_HIP: return "HIP runtime error";
     case VMOBA_ERR_OP: return "unknown op";
+    case VMOBA_ERR_SELECT: return "unknown selection mode or top-k count < 1";
     default: return "unknown status";
   }
 }

@@ -7,6 +7,7 @@
  *
  *   vmoba_partition_pool   block means of Q and K under the layer's 1D/2D/3D partition
  *   vmoba_select           per-head global block selection with the cumulative mass tau
+ *   vmoba_select_mode      the ablation's other selection strategies (top-k, local pools)
  *   vmoba_sparse_attn_fwd  attention restricted to the selected block pairs
  *   vmoba_sparse_attn_bwd  its gradient with the selection held constant
  *
@@ -58,7 +59,8 @@ typedef enum {
   VMOBA_ERR_WORKSPACE = 7,  /* ws too small (see vmoba_workspace_size)                 */
   VMOBA_ERR_OVERFLOW = 8,   /* an index or element count exceeds the int32 range used  */
   VMOBA_ERR_HIP = 9,        /* the HIP runtime reported an error at launch             */
-  VMOBA_ERR_OP = 10         /* unknown op in vmoba_workspace_size                      */
+  VMOBA_ERR_OP = 10,        /* unknown op in vmoba_workspace_size                      */
+  VMOBA_ERR_SELECT = 11     /* unknown selection mode, or top-k count k < 1            */
 } vmoba_status;
 
 typedef enum { VMOBA_BF16 = 0, VMOBA_FP32 = 1 } vmoba_dtype;
@@ -120,6 +122,33 @@ int vmoba_select(const vmoba_problem* p, const float* q_pool, const float* k_poo
                  float tau, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
                  int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
                  size_t ws_bytes, void* stream);
+
+/* Selection strategies.  THRESHOLD_GLOBAL is vmoba_select.  The other three are the
+ * strategies paperlayer §4.4 (Table 3) compares it with, each dropping one or both of its
+ * two ingredients:
+ *   TOPK_GLOBAL       the topk highest pairs of the head group's global pool;
+ *   THRESHOLD_LOCAL   every query-block row is its own pool, normalised by a softmax over
+ *                     the row; the shortest prefix of the row with mass >= tau;
+ *   TOPK_LOCAL        the topk highest key blocks of every query-block row (MoBA's rule).
+ * Order, ties (lower index first) and the forced diagonal are those of vmoba_select; a
+ * topk at least the pool size keeps the whole pool. */
+typedef enum {
+  VMOBA_SEL_THRESHOLD_GLOBAL = 0,
+  VMOBA_SEL_TOPK_GLOBAL = 1,
+  VMOBA_SEL_THRESHOLD_LOCAL = 2,
+  VMOBA_SEL_TOPK_LOCAL = 3
+} vmoba_selection;
+
+/* Block selection under `mode` (a vmoba_selection): tau is checked and used by the
+ * threshold modes (0 < tau <= 1), topk by the top-k modes (topk >= 1, else
+ * VMOBA_ERR_SELECT).  Outputs as vmoba_select; for the local modes head_stats = {sum
+ * over rows of the prefix lengths, nnz, mean over rows of the prefix mass, mean over rows
+ * of the smallest normalised score in the prefix} and norm_scores holds the
+ * row-normalised scores.  ws: vmoba_workspace_size(VMOBA_OP_SELECT) bytes. */
+int vmoba_select_mode(const vmoba_problem* p, const float* q_pool, const float* k_pool,
+                      int mode, float tau, int32_t topk, int32_t* row_ptr, int32_t* col_idx,
+                      int32_t* col_ptr, int32_t* row_idx, float* head_stats,
+                      float* norm_scores, void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention forward (papernotes 方法详解/整体框架; paperlayer §3.1): for every
  * query token x of query block i, O_x = softmax over the keys of the blocks listed in row

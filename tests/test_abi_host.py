@@ -189,3 +189,27 @@ def test_kernel_token_map_matches_oracle_blocks(geom_exe, lat, block):
     got = np.array(out.split(), dtype=np.int64)
     ref = oracle.block_members(*lat, block).reshape(-1)
     assert np.array_equal(got, ref)
+
+
+def test_select_mode_errors(L):
+    p = _prob()
+    bp = ctypes.byref(p)
+    args = lambda mode, tau, k, ws=FAKE, n=1 << 20: (bp, FAKE, FAKE, mode, tau, k, FAKE, FAKE,
+                                                     FAKE, FAKE, FAKE, NULL, ws, n, NULL)
+    assert L.vmoba_select_mode(*args(4, 0.25, 1)) == 11          # unknown mode
+    assert L.vmoba_select_mode(*args(-1, 0.25, 1)) == 11
+    for mode in (1, 3):                                           # top-k needs k >= 1
+        assert L.vmoba_select_mode(*args(mode, 0.25, 0)) == 11
+        assert L.vmoba_select_mode(*args(mode, 0.25, -5)) == 11
+        assert L.vmoba_select_mode(*args(mode, float("nan"), 3, FAKE, 16)) == 7   # tau unused
+    for mode in (0, 2):                                           # threshold needs a tau
+        for tau in (0.0, 1.5, float("nan")):
+            assert L.vmoba_select_mode(*args(mode, tau, 3)) == 4
+        assert L.vmoba_select_mode(*args(mode, 0.25, 0, FAKE, 16)) == 7           # k unused
+    assert L.vmoba_select_mode(*args(2, 0.25, 1, NULL, 1 << 20)) == 1
+    assert L.vmoba_status_string(11).decode().startswith("unknown selection mode")
+    # the local modes need the bitmap and row statistics behind the scores
+    n = ctypes.c_size_t(0)
+    assert L.vmoba_workspace_size(bp, 1, ctypes.byref(n)) == 0
+    nb, groups = 8, p.batch * p.heads
+    assert n.value >= groups * nb * nb * 4 + groups * nb * 4 + groups * nb * 12

@@ -108,3 +108,24 @@ def test_attention_full_size_sampled(layer):
     torch.cuda.synchronize()
     for a, b in zip((dq, dk, dv), g16):
         assert torch.equal(a.to(torch.bfloat16), b)
+
+
+def test_selection_modes_full_size(layer):
+    """The ablation's other strategies (top-k + global, threshold + local, top-k + local)
+    at full size: whole masks against the oracle, cutoff window exempt."""
+    from block_sparse_attention_layer_amd import vmoba_partition_pool, vmoba_select
+    from test_gpu_select_modes import _compare, _params
+    p, d = layer["p"], layer["dev"]
+    qp, kp = vmoba_partition_pool(p, d["q"], d["k"])
+    nb = layer["mem"].shape[0]
+    for mode in ("topk_global", "threshold_local", "topk_local"):
+        tau, k = _params(mode, nb)
+        sel = vmoba_select(p, qp, kp, tau, mode=mode, k=k)
+        torch.cuda.synchronize()
+        mask, shat, stats = oracle.select_all_heads(layer["qpool"], layer["kpool"], tau,
+                                                    mode=mode, k=k)
+        gm = masks_from_csr(sel.row_ptr, sel.col_idx, nb)
+        bad, exempt = _compare(mode, gm, mask, shat, stats)
+        print(f"  {mode} tau={tau} k={k} density={gm.mean():.4f} mismatches={bad} "
+              f"exempt={exempt}", flush=True)
+        assert bad == 0
