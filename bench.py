@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--topk", type=int, default=None, help="k of the top-k strategies")
     ap.add_argument("--sweep", action="store_true",
                     help="time every bf16 workload, layer and tau (one JSON line each)")
+    ap.add_argument("--sweep-workloads", default=None,
+                    help="comma-separated workloads for --sweep (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter scale)")
     return ap.parse_args()
@@ -320,7 +322,8 @@ def sweep(args):
     """One JSON line per workload layer and tau (the per-config report; not the contract
     line).  Fewer steps, no CPU sample."""
     from synthetic import CONFIGS, CONFIG_ORDER
-    for name in CONFIG_ORDER:
+    names = args.sweep_workloads.split(",") if args.sweep_workloads else CONFIG_ORDER
+    for name in names:
         cfg = CONFIGS[name]
         if cfg["dtype"] != "bf16":
             continue
