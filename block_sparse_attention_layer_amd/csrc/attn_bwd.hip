@@ -79,8 +79,10 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int LPW = QT / (NW * RPI);
   static_assert(QT % (NW * RPI) == 0, "tile rows split over waves");
   constexpr int TILE = QT * ROWB;
-  // per stage: Q tile, dO tile, then 2 x QT floats (lse * log2 e, delta)
-  constexpr int STAGE = 2 * TILE + 2 * QT * 4;
+  static_assert(NW >= 2 && QT <= 64, "LSE and delta are loaded by waves 0 and 1");
+  // per stage: Q tile, dO tile, then 64 floats of LSE and 64 of delta (one wave's load
+  // each; lanes 32-63 repeat the first 32)
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
 
   // two pipeline stages as separate objects (see the forward kernel)
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
@@ -106,9 +108,12 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
   GT* __restrict__ dK = static_cast<GT*>(a.dk);
   GT* __restrict__ dV = static_cast<GT*>(a.dv);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * D) * 2u;   // < 2^32 (validated)
+  const BufRes rQ = buffer_res(Q, tbytes), rO = buffer_res(dO, tbytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // the wave index, known uniform
   const int l32 = lane & 31, half = lane >> 5;
 
   int nq;
@@ -153,7 +158,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
       const int rrc = rr < klim ? rr : 0;
       const int32_t x = DENSE ? rrc : block_base(g, jblk) + block_offset(g, rrc);
       const int32_t off = row_offset(g, grp, x) + ((lane % CPR0) ^ swz<D>(r)) * 8;
-      load_to_lds16(V + off, vtile + (w * 32 + i * RPI) * ROWB);
+      load_to_lds16(buffer_res(V, tbytes), 2u * uint32_t(off), vtile + (w * 32 + i * RPI) * ROWB);
     }
   }
   const unsigned char* vrow = vtile;
@@ -168,6 +173,8 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 
   const float* lse_g = a.lse + size_t(grp) * g.L;
   const float* dl_g = a.delta + size_t(grp) * g.L;
+  const BufRes rL = buffer_res(lse_g, uint32_t(g.L) * 4u);
+  const BufRes rD = buffer_res(dl_g, uint32_t(g.L) * 4u);
   constexpr int CPR = D / 8;
   const int lrow0 = w * (QT / NW) + lane / CPR;
   const int lcp = lane % CPR;
@@ -196,13 +203,12 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int dst = (w * (QT / NW) + i * RPI) * ROWB;
-      load_to_lds16(Q + o[i], sb + dst);
-      load_to_lds16(dO + o[i], sb + TILE + dst);
+      load_to_lds16(rQ, 2u * uint32_t(o[i]), sb + dst);
+      load_to_lds16(rO, 2u * uint32_t(o[i]), sb + TILE + dst);
     }
-    if (w == 0) {   // lanes 0-31: lse of the tile's queries; lanes 32-63: delta
-      const float* src = half ? dl_g + xl : lse_g + xl;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(sb + 2 * TILE), 4, 0, 0);
-    }
+    // LSE and delta of the tile's queries; a scalar branch keeps the descriptors uniform
+    if (wu == 0) load_to_lds4(rL, 4u * uint32_t(xl), sb + 2 * TILE);
+    if (wu == 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + 64 * 4);
   };
   auto issue_tile = [&](int t, unsigned char* sb) {
     int32_t o[LPW], xl;
@@ -222,7 +228,7 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
     const unsigned char* qb = cur;
     const unsigned char* ob = cur + TILE;
     const float* lse_s = reinterpret_cast<const float*>(cur + 2 * TILE);
-    const float* dl_s = lse_s + QT;
+    const float* dl_s = lse_s + 64;
 
     f32x16 sacc, dpacc;
 #pragma unroll
@@ -354,6 +360,8 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
   GT* __restrict__ dQ = static_cast<GT*>(a.dq);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * D) * 2u;   // < 2^32 (validated)
+  const BufRes rK = buffer_res(K, tbytes), rV = buffer_res(V, tbytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -424,8 +432,8 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int dst = (w * (KT / NW) + i * RPI) * ROWB;
-      load_to_lds16(K + o[i], sb + dst);
-      load_to_lds16(V + o[i], sb + TILE + dst);
+      load_to_lds16(rK, 2u * uint32_t(o[i]), sb + dst);
+      load_to_lds16(rV, 2u * uint32_t(o[i]), sb + TILE + dst);
     }
   };
   int32_t noff[LPW];   // addresses of the next tile, computed one step ahead

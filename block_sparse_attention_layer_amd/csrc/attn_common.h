@@ -145,10 +145,33 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-// One wave instruction copies 64 x 16 bytes from global memory straight into the LDS
-// range [dst, dst + 1024); lane L's chunk lands at dst + 16 L.  `dst` must be uniform.
-__device__ __forceinline__ void load_to_lds16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+// Direct global->LDS loads go through buffer instructions.  The flat-addressed form
+// (global_load_lds) is one the compiler must assume may also touch LDS through the LDS
+// counter, so while any is in flight it waits for all of a wave's LDS reads at the first
+// use of any one of them; the buffer form is counted on the vector-memory counter only,
+// and the LDS reads that feed the matrix cores keep their one-by-one waits.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+// Word 3 of a CDNA buffer descriptor for raw addressing: 32-bit data format, no index
+// stride and no swizzle, so a lane's offset is a plain byte offset from the base.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Descriptor of the `bytes` bytes at `base` (reads past the end return zero).
+__device__ __forceinline__ BufRes buffer_res(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes),
+                                           kBufferWord3);
+}
+
+// One wave instruction copies 64 x 16 bytes straight into the LDS range
+// [dst, dst + 1024): lane L's chunk comes from byte `off` of the buffer and lands at
+// dst + 16 L.  `dst` must be uniform.
+__device__ __forceinline__ void load_to_lds16(BufRes r, uint32_t off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 16, off, 0, 0, 0);
+}
+
+// As load_to_lds16 with 4 bytes per lane: lane L's word lands at dst + 4 L.
+__device__ __forceinline__ void load_to_lds4(BufRes r, uint32_t off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 4, off, 0, 0, 0);
 }
 
 // Transposing LDS read: the 16 lanes of a group each name 8 bytes (4 bf16); lane i of

@@ -68,6 +68,8 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.out);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * g.D) * 2u;   // < 2^32 (validated)
+  const BufRes rK = buffer_res(K, tbytes), rV = buffer_res(V, tbytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -153,8 +155,8 @@ void attn_fwd_bf16_kernel(AttnParams a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int dst = (w * (KT / NW) + i * RPI) * ROWB;   // wave-uniform
-      load_to_lds16(K + o[i], smem + dst);
-      load_to_lds16(V + o[i], smem + TILE + dst);
+      load_to_lds16(rK, 2u * uint32_t(o[i]), smem + dst);
+      load_to_lds16(rV, 2u * uint32_t(o[i]), smem + TILE + dst);
     }
   };
   auto issue_tile = [&](int t, unsigned char* smem) {
@@ -395,6 +397,8 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.out);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * g.D) * 2u;   // < 2^32 (validated)
+  const BufRes rK = buffer_res(K, tbytes), rV = buffer_res(V, tbytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -475,8 +479,8 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int dst = (w * (KT / NW) + i * 4) * ROWB;   // wave-uniform
-      load_to_lds16(K + o[i] + kchunk[i], smem + dst);
-      load_to_lds16(V + o[i] + vchunk[i], smem + TILE + dst);
+      load_to_lds16(rK, 2u * uint32_t(o[i] + kchunk[i]), smem + dst);
+      load_to_lds16(rV, 2u * uint32_t(o[i] + vchunk[i]), smem + TILE + dst);
     }
   };
   auto issue_tile = [&](int t, unsigned char* smem) {
