@@ -11,10 +11,15 @@ from .api import (Problem, Selection, vmoba_dense_attn_bwd, vmoba_dense_attn_fwd
                   vmoba_sparse_attn_fwd, vmoba_validate,
                   vmoba_workspace_size)
 from ._lib import VMoBAError, lib
-from .layer import VMoBAAttention, vmoba_attention
+from .layer import (DenseAttention, VMoBAAttention, as_selection, full_attention,
+                    select_blocks, vmoba_attention)
+from .dit import (LayerCycle, SyntheticDiT, SyntheticDiTBlock, full_attention_step,
+                  num_full_steps)
 
 __all__ = [
-    "Problem", "Selection", "VMoBAError", "VMoBAAttention", "lib", "vmoba_attention",
+    "DenseAttention", "LayerCycle", "Problem", "Selection", "SyntheticDiT",
+    "SyntheticDiTBlock", "VMoBAError", "VMoBAAttention", "as_selection", "full_attention",
+    "full_attention_step", "lib", "num_full_steps", "select_blocks", "vmoba_attention",
     "vmoba_dense_attn_bwd", "vmoba_dense_attn_fwd", "vmoba_num_blocks",
     "vmoba_partition_pool", "vmoba_select", "vmoba_sparse_attn_bwd",
     "vmoba_sparse_attn_bwd_delta", "vmoba_sparse_attn_bwd_dkdv", "vmoba_sparse_attn_bwd_dq",

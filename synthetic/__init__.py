@@ -21,7 +21,8 @@ on the CPU and are then cast to the workload's dtype.
 """
 
 from .configs import CONFIGS, CONFIG_ORDER, LayerSpec, config_layers
+from .dit import PARAM_ORDER, make_dit_input, make_dit_params
 from .inputs import make_layer_inputs, seed_for
 
-__all__ = ["CONFIGS", "CONFIG_ORDER", "LayerSpec", "config_layers",
-           "make_layer_inputs", "seed_for"]
+__all__ = ["CONFIGS", "CONFIG_ORDER", "LayerSpec", "PARAM_ORDER", "config_layers",
+           "make_dit_input", "make_dit_params", "make_layer_inputs", "seed_for"]

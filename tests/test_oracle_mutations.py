@@ -123,3 +123,21 @@ def test_local_strict_inequality_is_caught(monkeypatch):
         return orig(shat_rows, tau=None if tau is None else np.nextafter(tau, 2.0), k=k)
     monkeypatch.setattr(oracle, "local_select", strict)
     assert _fails(t_modes.test_golden_local_and_topk_examples)
+
+
+def test_transposed_head_split_in_dit_block_is_caught(monkeypatch):
+    """Channels grouped into heads as [d, Hh] instead of [Hh, d]."""
+    import test_oracle_dit as t_dit
+    from oracle import dit as odit
+    orig = odit._OracleAttention.apply
+
+    def wrong(q, k, v, members, mask):
+        B, L, Hh, d = q.shape
+        to = lambda t: t.reshape(B, L, d, Hh).transpose(2, 3).contiguous()
+        a = orig(to(q), to(k), to(v), members, mask)
+        return a.transpose(2, 3).reshape(B, L, Hh, d)
+
+    assert not _fails(t_dit.test_heads_with_zero_query_key_average_selected_values, 2,
+                      (1, 2, 2))
+    monkeypatch.setattr(odit._OracleAttention, "apply", wrong)
+    assert _fails(t_dit.test_heads_with_zero_query_key_average_selected_values, 2, (1, 2, 2))
