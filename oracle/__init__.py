@@ -29,6 +29,10 @@ that takes it.  Modules:
   Table 3).
 * :mod:`oracle.attention` — masked softmax attention forward and backward
   (literal dense form, block-sparse form and sampled rows).
+* :mod:`oracle.tokens` — the token-granular query pool (every query token against every
+  key block) and the attention under its per-token selection.
+* :mod:`oracle.dit` — the layer inside a DiT block and stack (projections, MLP, the
+  1D/2D/3D layer cycle, the full-attention warm-up).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, library routines, invariants and brute force on tiny inputs.  The pages
@@ -51,6 +55,11 @@ from .attention import (
     sampled_key_block_grads,
 )
 from .layer import oracle_layer
+from .tokens import (
+    token_scores, normalise_token_pool, token_select, select_tokens_all_heads,
+    union_block_mask, token_level_mask, token_attention_fwd, token_attention_bwd,
+    sampled_token_rows,
+)
 
 __all__ = [
     "MODE_1D", "MODE_2D", "MODE_3D", "partition_mode", "check_partition",
@@ -60,5 +69,7 @@ __all__ = [
     "normalise_per_row", "local_select", "SELECTION_MODES",
     "dense_masked_attention_fwd", "dense_masked_attention_bwd", "token_mask",
     "sparse_attention_fwd", "sparse_attention_bwd", "sampled_query_rows",
-    "sampled_key_block_grads", "oracle_layer",
+    "sampled_key_block_grads", "oracle_layer", "token_scores", "normalise_token_pool",
+    "token_select", "select_tokens_all_heads", "union_block_mask", "token_level_mask",
+    "token_attention_fwd", "token_attention_bwd", "sampled_token_rows",
 ]

@@ -141,3 +141,43 @@ def test_transposed_head_split_in_dit_block_is_caught(monkeypatch):
                       (1, 2, 2))
     monkeypatch.setattr(odit._OracleAttention, "apply", wrong)
     assert _fails(t_dit.test_heads_with_zero_query_key_average_selected_values, 2, (1, 2, 2))
+
+
+def test_token_pool_normalised_per_token_is_caught(monkeypatch):
+    import test_oracle_tokens as t_tok
+    from oracle import tokens as otok
+
+    def per_token(s):
+        e = np.exp(s - s.max(axis=-1, keepdims=True))
+        return e / e.sum(axis=-1, keepdims=True)
+    assert not _fails(t_tok.test_pool_normalisation_sums_to_one)
+    monkeypatch.setattr(otok, "normalise_token_pool", per_token)
+    assert _fails(t_tok.test_pool_normalisation_sums_to_one)
+
+
+def test_token_ties_by_descending_index_are_caught(monkeypatch):
+    import test_oracle_tokens as t_tok
+    from oracle import tokens as otok
+
+    def desc_ties(vals, tau=None, k=None):
+        vals = np.asarray(vals, float)
+        n = vals.size
+        order = (n - 1 - np.argsort(-vals[::-1], kind="stable"))
+        hit = np.nonzero(np.cumsum(vals[order]) >= tau)[0]
+        return order, (int(hit[0]) + 1 if hit.size else n)
+    assert not _fails(t_tok.test_hand_worked_example_with_ties)
+    monkeypatch.setattr(otok, "_ordered_prefix", desc_ties)
+    assert _fails(t_tok.test_hand_worked_example_with_ties)
+
+
+def test_token_forced_pair_of_wrong_block_is_caught(monkeypatch):
+    import test_oracle_tokens as t_tok
+    from oracle import tokens as otok
+    orig = otok.token_select
+
+    def wrong_diag(shat, tau, blk_of_tok):
+        L, nb = np.asarray(shat).shape
+        return orig(shat, tau, np.arange(L) % nb)     # token index mod N_b, not its block
+    assert not _fails(t_tok.test_prefix_invariants, 1)
+    monkeypatch.setattr(otok, "token_select", wrong_diag)
+    assert _fails(t_tok.test_prefix_invariants, 1)
