@@ -4,7 +4,9 @@ The compute path is libvmoba.so (HIP kernels behind the C ABI of include/vmoba.h
 this package is its Python binding.
 """
 
-from .api import (Problem, Selection, vmoba_dense_attn_bwd, vmoba_dense_attn_fwd,
+from .api import (Problem, Selection, TokenSelection, vmoba_select_tokens,
+                  vmoba_token_attn_bwd, vmoba_token_attn_fwd,
+                  vmoba_dense_attn_bwd, vmoba_dense_attn_fwd,
                   vmoba_num_blocks, vmoba_partition_pool, vmoba_select,
                   vmoba_sparse_attn_bwd, vmoba_sparse_attn_bwd_delta,
                   vmoba_sparse_attn_bwd_dkdv, vmoba_sparse_attn_bwd_dq,
@@ -18,10 +20,11 @@ from .dit import (LayerCycle, SyntheticDiT, SyntheticDiTBlock, full_attention_st
 
 __all__ = [
     "DenseAttention", "LayerCycle", "Problem", "Selection", "SyntheticDiT",
-    "SyntheticDiTBlock", "VMoBAError", "VMoBAAttention", "as_selection", "full_attention",
+    "SyntheticDiTBlock", "TokenSelection", "VMoBAError", "VMoBAAttention", "as_selection", "full_attention",
     "full_attention_step", "lib", "num_full_steps", "select_blocks", "vmoba_attention",
     "vmoba_dense_attn_bwd", "vmoba_dense_attn_fwd", "vmoba_num_blocks",
     "vmoba_partition_pool", "vmoba_select", "vmoba_sparse_attn_bwd",
     "vmoba_sparse_attn_bwd_delta", "vmoba_sparse_attn_bwd_dkdv", "vmoba_sparse_attn_bwd_dq",
     "vmoba_sparse_attn_fwd", "vmoba_validate", "vmoba_workspace_size",
+    "vmoba_select_tokens", "vmoba_token_attn_fwd", "vmoba_token_attn_bwd",
 ]

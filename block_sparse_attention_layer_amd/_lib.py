@@ -15,11 +15,11 @@ STATUS_NAMES = {
     0: "VMOBA_OK", 1: "VMOBA_ERR_NULL", 2: "VMOBA_ERR_SHAPE", 3: "VMOBA_ERR_MODE",
     4: "VMOBA_ERR_TAU", 5: "VMOBA_ERR_DTYPE", 6: "VMOBA_ERR_HEAD_DIM",
     7: "VMOBA_ERR_WORKSPACE", 8: "VMOBA_ERR_OVERFLOW", 9: "VMOBA_ERR_HIP",
-    10: "VMOBA_ERR_OP",
+    10: "VMOBA_ERR_OP", 11: "VMOBA_ERR_SELECT",
 }
 VMOBA_BF16, VMOBA_FP32 = 0, 1
 OPS = {"pool": 0, "select": 1, "sparse_fwd": 2, "sparse_bwd": 3, "dense_fwd": 4,
-       "dense_bwd": 5}
+       "dense_bwd": 5, "select_tokens": 6, "token_fwd": 7, "token_bwd": 8}
 
 
 class CProblem(ctypes.Structure):
@@ -53,6 +53,12 @@ _SIG = {
     "vmoba_dense_attn_fwd": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, _P, _P, _P, _P,
                                             ctypes.c_size_t, _P]),
     "vmoba_dense_attn_bwd": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 10 +
+                             [ctypes.c_size_t, _P]),
+    "vmoba_select_tokens": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, ctypes.c_float] +
+                            [_P] * 7 + [ctypes.c_size_t, _P]),
+    "vmoba_token_attn_fwd": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 9 +
+                             [ctypes.c_size_t, _P]),
+    "vmoba_token_attn_bwd": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 15 +
                              [ctypes.c_size_t, _P]),
 }
 

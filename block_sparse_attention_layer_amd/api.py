@@ -304,3 +304,87 @@ def vmoba_dense_attn_bwd(p: Problem, q, k, v, o, lse, dout, dq=None, dk=None, dv
                                      _ptr(outs[2]), _ptr(ws), n, _stream(dev)),
           "vmoba_dense_attn_bwd")
     return tuple(outs)
+
+
+@dataclass
+class TokenSelection:
+    """Token-granular selection of every head group g = b*Hh + h (device tensors)."""
+    token_mask: torch.Tensor   # int32 bits [G, L, ceil(N_b/32)]: bit j%32 of word j//32
+    row_ptr: torch.Tensor      # union lists per query block (CSR), int32 [G, N_b+1]
+    col_idx: torch.Tensor      # int32 [G, N_b*N_b]
+    col_ptr: torch.Tensor      # and per key block (CSC)
+    row_idx: torch.Tensor
+    head_stats: torch.Tensor   # fp32 [G, 4]: k*, selected (token, block) pairs, mass, cutoff
+
+
+def _mask_shape(p, nb):
+    return (p.groups, p.L, (nb + 31) // 32)
+
+
+def vmoba_select_tokens(p: Problem, q, k_pool, tau: float) -> TokenSelection:
+    """Token-granular selection: the pool of a head is every (query token, key block)
+    pair; q [B, L, Hh, d] bf16, k_pool from vmoba_partition_pool."""
+    dev = q.device
+    nb = vmoba_num_blocks(p)
+    G = p.groups
+    _want(q, "q", _tok_shape(p), p.dtype, dev)
+    _want(k_pool, "k_pool", (p.batch, p.heads, nb, p.head_dim), torch.float32, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    sel = TokenSelection(
+        token_mask=torch.empty(_mask_shape(p, nb), **i32),
+        row_ptr=torch.empty((G, nb + 1), **i32), col_idx=torch.empty((G, nb * nb), **i32),
+        col_ptr=torch.empty((G, nb + 1), **i32), row_idx=torch.empty((G, nb * nb), **i32),
+        head_stats=torch.empty((G, 4), dtype=torch.float32, device=dev))
+    ws, n = _workspace(p, "select_tokens", dev)
+    s = p.c_struct()
+    check(lib().vmoba_select_tokens(ctypes.byref(s), _ptr(q), _ptr(k_pool), ctypes.c_float(tau),
+                                    _ptr(sel.token_mask), _ptr(sel.row_ptr), _ptr(sel.col_idx),
+                                    _ptr(sel.col_ptr), _ptr(sel.row_idx), _ptr(sel.head_stats),
+                                    _ptr(ws), n, _stream(dev)), "vmoba_select_tokens")
+    return sel
+
+
+def vmoba_token_attn_fwd(p: Problem, q, k, v, row_ptr, col_idx, token_mask, o=None, lse=None):
+    dev = q.device
+    nb = vmoba_num_blocks(p)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _want(t, name, _tok_shape(p), p.dtype, dev)
+    _check_lists(p, dev, ("row_ptr", row_ptr, lambda n: n + 1),
+                 ("col_idx", col_idx, lambda n: n * n))
+    _want(token_mask, "token_mask", _mask_shape(p, nb), torch.int32, dev)
+    o = torch.empty(_tok_shape(p), dtype=p.dtype, device=dev) if o is None else o
+    lse = torch.empty((p.batch, p.heads, p.L), dtype=torch.float32, device=dev) if lse is None else lse
+    _want(o, "o", _tok_shape(p), p.dtype, dev)
+    _want(lse, "lse", (p.batch, p.heads, p.L), torch.float32, dev)
+    ws, n = _workspace(p, "token_fwd", dev)
+    s = p.c_struct()
+    check(lib().vmoba_token_attn_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                     _ptr(col_idx), _ptr(token_mask), _ptr(o), _ptr(lse),
+                                     _ptr(ws), n, _stream(dev)), "vmoba_token_attn_fwd")
+    return o, lse
+
+
+def vmoba_token_attn_bwd(p: Problem, q, k, v, o, lse, dout, row_ptr, col_idx, col_ptr,
+                         row_idx, token_mask, dq=None, dk=None, dv=None):
+    dev = q.device
+    nb = vmoba_num_blocks(p)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _want(t, name, _tok_shape(p), p.dtype, dev)
+    _want(lse, "lse", (p.batch, p.heads, p.L), torch.float32, dev)
+    _check_lists(p, dev, ("row_ptr", row_ptr, lambda n: n + 1),
+                 ("col_idx", col_idx, lambda n: n * n),
+                 ("col_ptr", col_ptr, lambda n: n + 1),
+                 ("row_idx", row_idx, lambda n: n * n))
+    _want(token_mask, "token_mask", _mask_shape(p, nb), torch.int32, dev)
+    outs = [torch.empty(_tok_shape(p), dtype=p.gdtype, device=dev) if t is None else t
+            for t in (dq, dk, dv)]
+    for name, t in zip(("dq", "dk", "dv"), outs):
+        _want(t, name, _tok_shape(p), p.gdtype, dev)
+    ws, n = _workspace(p, "token_bwd", dev)
+    s = p.c_struct()
+    check(lib().vmoba_token_attn_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(lse), _ptr(dout), _ptr(row_ptr), _ptr(col_idx),
+                                     _ptr(col_ptr), _ptr(row_idx), _ptr(token_mask),
+                                     _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(ws), n,
+                                     _stream(dev)), "vmoba_token_attn_bwd")
+    return tuple(outs)

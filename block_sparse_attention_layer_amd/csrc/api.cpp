@@ -25,6 +25,19 @@ int check_ws(const vmoba_problem* p, int op, const void* ws, size_t ws_bytes) {
   return VMOBA_OK;
 }
 
+// Token-granular calls: bf16, N_b <= kMaxBlocks, and the mask and score tables within the
+// 32-bit ranges the kernels use.
+int check_tokens(const vmoba_problem* p) {
+  if (p->dtype != VMOBA_BF16) return VMOBA_ERR_DTYPE;
+  const Geom g = make_geom(p);
+  if (g.Nb > kMaxBlocks) return VMOBA_ERR_SHAPE;
+  const int64_t G = int64_t(g.B) * g.Hh;
+  const int64_t words = (int64_t(g.Nb) + 31) / 32;
+  if (G * g.L * g.Nb >= (int64_t(1) << 31) || G * g.L * words * 4 >= (int64_t(1) << 32))
+    return VMOBA_ERR_OVERFLOW;
+  return VMOBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,6 +180,67 @@ int vmoba_dense_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
                             stream)))
     return st;
   return launch_bwd_dq(g, true, q, k, v, lse, delta, dout, nullptr, nullptr, dq, stream);
+}
+
+int vmoba_select_tokens(const vmoba_problem* p, const void* q, const float* k_pool, float tau,
+                        uint32_t* token_mask, int32_t* row_ptr, int32_t* col_idx,
+                        int32_t* col_ptr, int32_t* row_idx, float* head_stats, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_tokens(p))) return st;
+  if (!(tau > 0.0f) || !(tau <= 1.0f) || !isfinite(tau)) return VMOBA_ERR_TAU;
+  if (!q || !k_pool || !token_mask || !row_ptr || !col_idx || !col_ptr || !row_idx ||
+      !head_stats)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_SELECT_TOKENS, ws, ws_bytes))) return st;
+  return launch_select_tokens(make_geom(p), q, k_pool, tau, token_mask, row_ptr, col_idx,
+                              col_ptr, row_idx, head_stats, ws, stream);
+}
+
+int vmoba_token_attn_fwd(const vmoba_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const uint32_t* token_mask, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_tokens(p))) return st;
+  if (make_geom(p).S < 4) return VMOBA_ERR_SHAPE;
+  if (!q || !k || !v || !row_ptr || !col_idx || !token_mask || !o || !lse)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_TOKEN_FWD, ws, ws_bytes))) return st;
+  const Geom g = make_geom(p);
+  uint32_t* posmask = static_cast<uint32_t*>(ws);
+  if ((st = launch_token_posmask(g, row_ptr, col_idx, token_mask, posmask, stream))) return st;
+  return launch_token_attn_fwd(g, q, k, v, row_ptr, col_idx, posmask, o, lse, stream);
+}
+
+int vmoba_token_attn_bwd(const vmoba_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const int32_t* col_ptr, const int32_t* row_idx,
+                         const uint32_t* token_mask, void* dq, void* dk, void* dv, void* ws,
+                         size_t ws_bytes, void* stream) {
+  int st = check_common(p);
+  if (st) return st;
+  if ((st = check_tokens(p))) return st;
+  if (make_geom(p).S < 4) return VMOBA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse || !dout || !row_ptr || !col_idx || !col_ptr ||
+      !row_idx || !token_mask || !dq || !dk || !dv)
+    return VMOBA_ERR_NULL;
+  if ((st = check_ws(p, VMOBA_OP_TOKEN_BWD, ws, ws_bytes))) return st;
+  const Geom g = make_geom(p);
+  const size_t words = (size_t(g.Nb) + 31) / 32;
+  uint32_t* posmask = static_cast<uint32_t*>(ws);
+  float* delta = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) +
+                                          align256(size_t(g.B) * g.Hh * g.L * words * 4));
+  if ((st = launch_token_posmask(g, row_ptr, col_idx, token_mask, posmask, stream))) return st;
+  if ((st = launch_bwd_delta(g, o, dout, delta, stream))) return st;
+  if ((st = launch_token_bwd_dkdv(g, q, k, v, lse, delta, dout, col_ptr, row_idx, token_mask,
+                                  dk, dv, stream)))
+    return st;
+  return launch_token_bwd_dq(g, q, k, v, lse, delta, dout, row_ptr, col_idx, posmask, dq,
+                             stream);
 }
 
 }  // extern "C"

@@ -69,7 +69,9 @@ __device__ __forceinline__ void store4(GT* dst, float a, float b, float c, float
 
 // ---------------------------------------------------------------------------------
 // dK, dV: one wave per 32 keys, query stream from the column list of the key block.
-template <int D, int NW, bool DENSE, bool TAB, typename GT>
+// TOK: token-granular selection, a query token's pairs with this key block kept only where
+// its key-block mask has the block's bit.
+template <int D, int NW, bool DENSE, bool TAB, typename GT, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -79,10 +81,10 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   constexpr int LPW = QT / (NW * RPI);
   static_assert(QT % (NW * RPI) == 0, "tile rows split over waves");
   constexpr int TILE = QT * ROWB;
-  static_assert(NW >= 2 && QT <= 64, "LSE and delta are loaded by waves 0 and 1");
+  static_assert(NW >= 3 && QT <= 64, "LSE, delta and mask words are loaded by waves 0-2");
   // per stage: Q tile, dO tile, then 64 floats of LSE and 64 of delta (one wave's load
-  // each; lanes 32-63 repeat the first 32)
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 4;
+  // each; lanes 32-63 repeat the first 32), and with TOK 64 mask words
+  constexpr int STAGE = 2 * TILE + (TOK ? 3 : 2) * 64 * 4;
 
   // two pipeline stages as separate objects (see the forward kernel)
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
@@ -175,6 +177,9 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   const float* dl_g = a.delta + size_t(grp) * g.L;
   const BufRes rL = buffer_res(lse_g, uint32_t(g.L) * 4u);
   const BufRes rD = buffer_res(dl_g, uint32_t(g.L) * 4u);
+  // key-block mask words: G * L * mwords * 4 < 2^32 bytes (validated)
+  const BufRes rM = buffer_res(a.tokmask, uint32_t(g.B * g.Hh * g.L * a.mwords) * 4u);
+  const uint32_t mword = uint32_t(grp * g.L) * uint32_t(a.mwords) + uint32_t(jblk >> 5);
   constexpr int CPR = D / 8;
   const int lrow0 = w * (QT / NW) + lane / CPR;
   const int lcp = lane % CPR;
@@ -209,6 +214,10 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
     // LSE and delta of the tile's queries; a scalar branch keeps the descriptors uniform
     if (wu == 0) load_to_lds4(rL, 4u * uint32_t(xl), sb + 2 * TILE);
     if (wu == 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + 64 * 4);
+    if constexpr (TOK)
+      if (wu == 2)
+        load_to_lds4(rM, 4u * (mword + uint32_t(xl) * uint32_t(a.mwords)),
+                     sb + 2 * TILE + 2 * 64 * 4);
   };
   auto issue_tile = [&](int t, unsigned char* sb) {
     int32_t o[LPW], xl;
@@ -270,6 +279,20 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
           dpacc[v] = 0.f;
         }
     }
+    if constexpr (TOK) {   // queries that did not select this key block: no P, no dS
+      const uint32_t* mk_s = reinterpret_cast<const uint32_t*>(cur + 2 * TILE + 2 * 64 * 4);
+      const uint32_t jb = uint32_t(jblk) & 31u;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const u32x4 m4 = *reinterpret_cast<const u32x4*>(mk_s + gq * 8 + half * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!((m4[r] >> jb) & 1u)) {
+            sacc[4 * gq + r] = 0.f;
+            dpacc[4 * gq + r] = 0.f;
+          }
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int g0 = ks * 8;
@@ -328,7 +351,8 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 
 // ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
-template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT>
+// TOK: token-granular selection, as in the forward (list-position mask of the query).
+template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -400,6 +424,8 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   }
   const float lse2 = a.lse[size_t(grp) * g.L + xq] * kLog2e;
   const float dl = a.delta[size_t(grp) * g.L + xq];
+  // token-granular selection: this lane's row of the list-position mask
+  const uint32_t pmrow = uint32_t(grp * g.L + xq) * uint32_t(a.mwords);
 
   f32x16 dqacc[D / 32];
 #pragma unroll
@@ -445,11 +471,42 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
     unsigned char* const cur = ST ? stage1 : stage0;
     unsigned char* const nxt = ST ? stage0 : stage1;
+    // the two mask words of this tile, loaded before the next tile's loads are issued so
+    // that waiting for them does not wait for those
+    uint32_t pw0 = 0u, pw1 = 0u;
+    if constexpr (TOK) {
+      const int wi = int(fd_div(uint32_t(t * KT), g.div_S)) >> 5;
+      pw0 = wi < a.mwords ? a.posmask[pmrow + wi] : 0u;
+      pw1 = wi + 1 < a.mwords ? a.posmask[pmrow + wi + 1] : 0u;
+    }
     if (t + 1 < ntiles) {
       issue_offsets(noff, nxt);
       tile_offsets(t + 2, noff);
     }
     if (wave_busy) {
+    // token-granular selection: which of this lane's keys its query selected, worked out
+    // before the products take the registers (one bit per key)
+    uint32_t keepbits = ~0u;
+    if constexpr (TOK) {
+      keepbits = 0u;
+      const uint32_t p0 = uint32_t(t * KT);
+      const int wi = int(fd_div(p0, g.div_S)) >> 5;
+      const uint32_t w0 = pw0, w1 = pw1;
+      // opaque per-tile base: otherwise the 16 per-key lane offsets are hoisted out of the
+      // loop into 16 registers
+      uint32_t pb = p0 + 4 * half;
+      asm volatile("" : "+v"(pb));
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t p = pb + (kk * 32 + 8 * (v >> 2) + (v & 3));
+          const int rel = int(fd_div(p, g.div_S)) - 32 * wi;
+          keepbits |= ((((rel < 32) ? w0 : w1) >> (rel & 31)) & 1u) << (kk * 16 + v);
+        }
+      // keep the computation here: sunk to its use it lands where registers are scarcest
+      asm volatile("" : "+v"(keepbits));
+    }
     const unsigned char* kb = cur;
     const unsigned char* vb = cur + TILE;
     // While direct-to-LDS loads are in flight the compiler waits for every outstanding LDS
@@ -464,9 +521,10 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
         sacc[kk][v] = 0.f;
         dpacc[kk][v] = 0.f;
       }
+    constexpr int NB = TOK ? 4 : 2;   // batches (more, smaller ones with the token mask)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      constexpr int HS = D / 32;   // d-steps per batch
+    for (int hb = 0; hb < NB; ++hb) {
+      constexpr int HS = D / 16 / NB;   // d-steps per batch
       bf16x8 ka[KSUB][HS], va[KSUB][HS];
 #pragma unroll
       for (int kk = 0; kk < KSUB; ++kk)
@@ -514,6 +572,13 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (t * KT + kk * 32 + 8 * (v >> 2) + 4 * half + (v & 3) >= nkeys) dpacc[kk][v] = 0.f;
+    }
+    if constexpr (TOK) {   // list positions this lane's query did not select: no dS
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (!((keepbits >> (kk * 16 + v)) & 1u)) dpacc[kk][v] = 0.f;
     }
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
@@ -732,7 +797,7 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
                                          static_cast<const T*>(dout), delta);
 }
 
-template <int D, bool DENSE, typename GT>
+template <int D, bool DENSE, typename GT, bool TOK = false>
 static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int NWK = 4;
@@ -741,12 +806,12 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
   const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, !DENSE, GT><<<grid, NWK * 64, 0, s>>>(a);
+    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, !DENSE, GT, TOK><<<grid, NWK * 64, 0, s>>>(a);
   else
-    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, false, GT><<<grid, NWK * 64, 0, s>>>(a);
+    attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, false, GT, TOK><<<grid, NWK * 64, 0, s>>>(a);
 }
 
-template <int D, bool DENSE, typename GT>
+template <int D, bool DENSE, typename GT, bool TOK = false>
 static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int KSUB = D == 128 ? 1 : 2;   // staging needs KSUB*32*D/8 to split over 4 waves
@@ -755,9 +820,9 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   a.tiles = (lim + 127) / 128;
   const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK><<<grid, 256, 0, s>>>(a);
   else
-    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT, TOK><<<grid, 256, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>
@@ -850,6 +915,53 @@ int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const
   a.dq = dq;
   if (g.dtype == VMOBA_BF16) VMOBA_DISPATCH_BF16(launch_dq_bf16, a, s, dense);
   else VMOBA_DISPATCH_F32(launch_dq_f32, a, s, dense);
+  return launch_status();
+}
+
+// Token-granular selection: dK/dV over the column lists under the key-block mask, dQ over
+// the row lists under the list-position mask (bf16 only).
+int launch_token_bwd_dkdv(const Geom& g, const void* q, const void* k, const void* v,
+                          const float* lse, const float* delta, const void* dout,
+                          const int32_t* col_ptr, const int32_t* row_idx,
+                          const uint32_t* tokmask, void* dk, void* dv, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a = bwd_params(g, q, k, v, lse, delta, dout);
+  a.col_ptr = col_ptr;
+  a.row_idx = row_idx;
+  a.tokmask = tokmask;
+  a.mwords = (g.Nb + 31) / 32;
+  a.dk = dk;
+  a.dv = dv;
+  const bool g32 = g.grad_dtype == VMOBA_FP32;
+  if (g.D == 128) {
+    if (g32) launch_dkdv_bf16<128, false, float, true>(a, s);
+    else launch_dkdv_bf16<128, false, uint16_t, true>(a, s);
+  } else {
+    if (g32) launch_dkdv_bf16<64, false, float, true>(a, s);
+    else launch_dkdv_bf16<64, false, uint16_t, true>(a, s);
+  }
+  return launch_status();
+}
+
+int launch_token_bwd_dq(const Geom& g, const void* q, const void* k, const void* v,
+                        const float* lse, const float* delta, const void* dout,
+                        const int32_t* row_ptr, const int32_t* col_idx,
+                        const uint32_t* posmask, void* dq, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a = bwd_params(g, q, k, v, lse, delta, dout);
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.posmask = posmask;
+  a.mwords = (g.Nb + 31) / 32;
+  a.dq = dq;
+  const bool g32 = g.grad_dtype == VMOBA_FP32;
+  if (g.D == 128) {
+    if (g32) launch_dq_bf16<128, false, float, true>(a, s);
+    else launch_dq_bf16<128, false, uint16_t, true>(a, s);
+  } else {
+    if (g32) launch_dq_bf16<64, false, float, true>(a, s);
+    else launch_dq_bf16<64, false, uint16_t, true>(a, s);
+  }
   return launch_status();
 }
 

@@ -33,6 +33,41 @@ struct AttnParams {
   int32_t tiles;       // tiles per block row (query tiles fwd/dq, key tiles dkdv)
   float scale;         // 1/sqrt(d)
   float scale_log2;    // log2(e)/sqrt(d)
+  // token-granular selection: per query token, bits over key blocks (tokmask) and over the
+  // positions of its block's list (posmask); mwords = ceil(N_b/32) words per token
+  const uint32_t* tokmask;
+  const uint32_t* posmask;
+  int32_t mwords;
+};
+
+// A query token's row of the list-position mask (bit li of word li >> 5: the li-th key
+// block listed for its query block is attended).  A key tile covers fewer than 32 list
+// positions (blocks of at least 4 tokens, tiles of at most 64 keys), so two cached words
+// serve a tile; they are refetched when the tile's first position enters another word.
+struct PosMask {
+  const uint32_t* row;
+  int W, wi;
+  uint32_t w0, w1;
+  __device__ __forceinline__ void init(const uint32_t* r, int words) {
+    row = r;
+    W = words;
+    wi = -1;
+    w0 = w1 = 0u;
+  }
+  __device__ __forceinline__ void fetch(int li0) {
+    const int n = li0 >> 5;
+    if (n != wi) {
+      wi = n;
+      w0 = n < W ? row[n] : 0u;
+      w1 = n + 1 < W ? row[n + 1] : 0u;
+    }
+  }
+  // positions past the cached pair (keys past the stream's end) read garbage bits; the
+  // ragged-tile mask covers them
+  __device__ __forceinline__ bool keep(int li) const {
+    const int rel = li - 32 * wi;
+    return (((rel < 32) ? w0 : w1) >> (rel & 31)) & 1u;
+  }
 };
 
 // The dispatcher hands workgroup b to XCD b % 8, and each XCD has its own L2; all XCDs

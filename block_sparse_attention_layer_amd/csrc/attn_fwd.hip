@@ -23,7 +23,9 @@
 
 namespace vmoba {
 
-template <int D, int NW, int KSUB, int NS, bool DENSE, bool TAB>
+// TOK: token-granular selection, the keys of list position li kept only where bit li of
+// the query token's position-mask row is set.
+template <int D, int NW, int KSUB, int NS, bool DENSE, bool TAB, bool TOK = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -108,6 +110,8 @@ void attn_fwd_bf16_kernel(AttnParams a) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
     qf[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + qoff + s * 16 + half * 8));
+  PosMask pm;
+  if constexpr (TOK) pm.init(a.posmask + (size_t(grp) * g.L + xq) * a.mwords, a.mwords);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -200,6 +204,22 @@ void attn_fwd_bf16_kernel(AttnParams a) {
         }
     }
   };
+  // token-granular selection: keys of list positions this lane's query did not select
+  auto mask_tokens = [&](f32x16 (&acc)[KSUB], int t) {
+    if constexpr (TOK) {
+      const uint32_t p0 = uint32_t(t * KT);
+      pm.fetch(int(fd_div(p0, g.div_S)));
+      uint32_t pb = p0 + 4 * half;   // opaque, so the per-key offsets are not hoisted
+      asm volatile("" : "+v"(pb));
+#pragma unroll
+      for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t p = pb + (kt * 32 + 8 * (v >> 2) + (v & 3));
+          if (!pm.keep(int(fd_div(p, g.div_S)))) acc[kt][v] = -INFINITY;
+        }
+    }
+  };
   // max over the tile's keys of this lane's query: the lane's own 16*KSUB scores, then the
   // other lane half (lane l ^ 32 holds the other keys of the same query)
   auto tile_max = [&](const f32x16 (&acc)[KSUB]) -> float {
@@ -218,7 +238,9 @@ void attn_fwd_bf16_kernel(AttnParams a) {
     const bool grow = mx > m_run + thr;
     if (__ballot(grow)) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      // (with token masks a lane that has seen only masked keys keeps m = -inf, and
+      // -inf - -inf would make its alpha NaN)
+      const float alpha = (TOK && !grow) ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
@@ -229,7 +251,8 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   };
   // P = exp2(S c2 - m c2), summed into l and packed to bf16 pairs (B operand of O^T += V^T P^T)
   auto softmax_pack = [&](const f32x16 (&acc)[KSUB], u32x4 (&pw)[2 * KSUB]) {
-    const float moff = m_run * c2;
+    // (with token masks a query may have seen only masked keys so far: m = -inf, P = 0)
+    const float moff = (TOK && m_run == -INFINITY) ? 0.f : m_run * c2;
     float psum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
@@ -282,6 +305,7 @@ void attn_fwd_bf16_kernel(AttnParams a) {
       bf16x8 kf[KSUB][D / 16];
       load_k(stage(std::integral_constant<int, ST + 1>{}), kf);
       mask_tail(cur, t);
+      mask_tokens(cur, t);
       maybe_rescale(tile_max(cur));
       u32x4 pw[2 * KSUB];
       scores(kf, nxt);
@@ -318,7 +342,7 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   // is released
   wait_vmcnt_lds<0>();
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const bool empty = nkeys == 0;
+  const bool empty = nkeys == 0 || (TOK && !(l_tot > 0.f));
   const float inv = empty ? 0.f : 1.0f / l_tot;
   if (qvalid) {
 #pragma unroll
@@ -736,7 +760,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams a) {
   }
 }
 
-template <int D, int NW, int KSUB, int NS, bool DENSE>
+template <int D, int NW, int KSUB, int NS, bool DENSE, bool TOK = false>
 static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const Geom& g = a.g;
   const int qlim = DENSE ? g.L : g.S;
@@ -744,9 +768,9 @@ static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const int rows = DENSE ? 1 : g.Nb;
   const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, !DENSE><<<grid, NW * 64, 0, s>>>(a);
+    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, !DENSE, TOK><<<grid, NW * 64, 0, s>>>(a);
   else
-    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, false><<<grid, NW * 64, 0, s>>>(a);
+    attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, false, TOK><<<grid, NW * 64, 0, s>>>(a);
 }
 
 template <int M, bool DENSE>
@@ -813,6 +837,74 @@ int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
       else launch_fwd_f32<64, false>(a, s);
     }
   }
+  return launch_status();
+}
+
+// Token-granular selection: the list-position mask of every query token from its key-block
+// mask and its block's list (entries outside [0, N_b) skipped, as the attention kernels
+// skip them).  One wave per token; bits are gathered in LDS, then written as whole words.
+__global__ __launch_bounds__(256) void token_posmask_kernel(Geom g, const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ col_idx,
+                                                            const uint32_t* __restrict__ tokmask,
+                                                            uint32_t* __restrict__ posmask) {
+  __shared__ uint32_t words[4][kMaxBlocks / 32];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int grp = blockIdx.y;
+  const int x = blockIdx.x * 4 + w;
+  const int W = (g.Nb + 31) / 32;
+  for (int i = lane; i < W; i += 64) words[w][i] = 0u;
+  __syncthreads();
+  if (x < g.L) {
+    const int blk = token_block(g, x);
+    int start, len;
+    list_range(g, row_ptr, grp, blk, &start, &len);
+    const int32_t* lst = col_idx + size_t(grp) * g.Nb * g.Nb + start;
+    const uint32_t* tm = tokmask + (size_t(grp) * g.L + x) * W;
+    int pos = 0;
+    for (int base = 0; base < len; base += 64) {
+      const int i = base + lane;
+      const int32_t j = i < len ? lst[i] : -1;
+      const bool ok = j >= 0 && j < g.Nb;
+      const unsigned long long vm = __ballot(ok);
+      const int li = pos + __popcll(vm & ((1ull << lane) - 1ull));
+      if (ok && ((tm[j >> 5] >> (j & 31)) & 1u)) atomicOr(&words[w][li >> 5], 1u << (li & 31));
+      pos += __popcll(vm);
+    }
+  }
+  __syncthreads();
+  if (x < g.L) {
+    uint32_t* dst = posmask + (size_t(grp) * g.L + x) * W;
+    for (int i = lane; i < W; i += 64) dst[i] = words[w][i];
+  }
+}
+
+int launch_token_posmask(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx,
+                         const uint32_t* tokmask, uint32_t* posmask, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((g.L + 3) / 4, g.B * g.Hh);
+  token_posmask_kernel<<<grid, 256, 0, s>>>(g, row_ptr, col_idx, tokmask, posmask);
+  return launch_status();
+}
+
+int launch_token_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                          const int32_t* row_ptr, const int32_t* col_idx,
+                          const uint32_t* posmask, void* o, float* lse, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnParams a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = o;
+  a.lse = lse;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.posmask = posmask;
+  a.mwords = (g.Nb + 31) / 32;
+  a.scale = 1.0f / sqrtf(float(g.D));
+  a.scale_log2 = kLog2e * a.scale;
+  if (g.D == 128) launch_fwd_bf16<128, 4, 1, 4, false, true>(a, s);
+  else launch_fwd_bf16<64, 4, 2, 4, false, true>(a, s);
   return launch_status();
 }
 

@@ -62,6 +62,14 @@ VMOBA_HD int32_t block_base(const Geom& g, uint32_t j) {
   return int32_t((jt * g.bt * g.H + jh * g.bh) * g.W + jw * g.bw);
 }
 
+// Block of token x (inverse of base + offset).
+VMOBA_HD int32_t token_block(const Geom& g, int32_t x) {
+  const int32_t hw = g.H * g.W;
+  const int32_t t = x / hw, rem = x - t * hw;
+  const int32_t h = rem / g.W, w = rem - h * g.W;
+  return ((t / g.bt) * g.nh + h / g.bh) * g.nw + w / g.bw;
+}
+
 VMOBA_HD int32_t block_offset(const Geom& g, uint32_t r) {
   uint32_t dt = fd_div(r, g.div_bhbw);
   uint32_t rem = r - dt * uint32_t(g.bh * g.bw);

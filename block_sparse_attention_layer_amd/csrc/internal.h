@@ -31,6 +31,29 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
                   int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
                   void* stream);
 
+// Token-granular selection (select.hip); token_select_ws is its workspace size.
+size_t token_select_ws(const Geom& g);
+int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, float tau,
+                         uint32_t* tokmask, int32_t* row_ptr, int32_t* col_idx,
+                         int32_t* col_ptr, int32_t* row_idx, float* head_stats, void* ws,
+                         void* stream);
+
+// Attention under a token mask (attn_fwd.hip / attn_bwd.hip, bf16): the list-position
+// mask from the key-block mask, the forward, and the two gradient kernels.
+int launch_token_posmask(const Geom& g, const int32_t* row_ptr, const int32_t* col_idx,
+                         const uint32_t* tokmask, uint32_t* posmask, void* stream);
+int launch_token_attn_fwd(const Geom& g, const void* q, const void* k, const void* v,
+                          const int32_t* row_ptr, const int32_t* col_idx,
+                          const uint32_t* posmask, void* o, float* lse, void* stream);
+int launch_token_bwd_dkdv(const Geom& g, const void* q, const void* k, const void* v,
+                          const float* lse, const float* delta, const void* dout,
+                          const int32_t* col_ptr, const int32_t* row_idx,
+                          const uint32_t* tokmask, void* dk, void* dv, void* stream);
+int launch_token_bwd_dq(const Geom& g, const void* q, const void* k, const void* v,
+                        const float* lse, const float* delta, const void* dout,
+                        const int32_t* row_ptr, const int32_t* col_idx,
+                        const uint32_t* posmask, void* dq, void* stream);
+
 int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
                     const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                     void* o, float* lse, void* ws, void* stream);

@@ -106,7 +106,8 @@ struct SelShared {
 // wave that share a digit (typical for the leading digit, whose bits hold the sign and
 // exponent) are summed first and added by one leader; after four rounds the remaining
 // lanes, whose digits are spread out, add directly.
-__device__ __forceinline__ void histogram_add(SelShared& sh, bool match, uint32_t dg,
+__device__ __forceinline__ void histogram_add(uint32_t* cnt, unsigned long long* hmass,
+                                              bool match, uint32_t dg,
                                               unsigned long long mass) {
   const int lane = threadIdx.x & 63;
   unsigned long long active = __ballot(match);
@@ -117,16 +118,21 @@ __device__ __forceinline__ void histogram_add(SelShared& sh, bool match, uint32_
     const unsigned long long smask = __ballot(same);
     const unsigned long long msum = wave_sum_u64(same ? mass : 0ull);
     if (lane == leader) {
-      atomicAdd(&sh.cnt[ldg], uint32_t(__popcll(smask)));
-      atomicAdd(&sh.mass[ldg], msum);
+      atomicAdd(&cnt[ldg], uint32_t(__popcll(smask)));
+      atomicAdd(&hmass[ldg], msum);
     }
     match = match && !same;
     active &= ~smask;
   }
   if (match) {
-    atomicAdd(&sh.cnt[dg], 1u);
-    atomicAdd(&sh.mass[dg], mass);
+    atomicAdd(&cnt[dg], 1u);
+    atomicAdd(&hmass[dg], mass);
   }
+}
+
+__device__ __forceinline__ void histogram_add(SelShared& sh, bool match, uint32_t dg,
+                                              unsigned long long mass) {
+  histogram_add(sh.cnt, sh.mass, match, dg, mass);
 }
 
 __device__ float block_max(float v, SelShared& sh) {
@@ -464,7 +470,7 @@ __global__ __launch_bounds__(256) void select_local_kernel(
 
 // CSR and CSC of one head group from a row-aligned pair bitmap (N_b rows of
 // ceil(N_b/32) words), plus head_stats = {sum of prefix lengths, nnz, mean prefix mass,
-// mean smallest prefix score} over the rows.
+// mean smallest prefix score} over the rows (rowstats and head_stats may be null).
 __global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
     int Nb, const uint32_t* __restrict__ bitmap, const float* __restrict__ rowstats,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
   int32_t* rp = row_ptr + size_t(grp) * (Nb + 1);
   int32_t* cp = col_ptr + size_t(grp) * (Nb + 1);
   float ks = 0.f, ms = 0.f, vsum = 0.f;
-  for (int i = tid; i < Nb; i += kSelThreads) {
+  for (int i = tid; i < Nb && rowstats; i += kSelThreads) {
     const float* rs = rowstats + (size_t(grp) * Nb + i) * 3;
     ks += rs[0];
     ms += rs[1];
@@ -556,6 +562,324 @@ __global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
       if (bit(j, i)) ri[pc++] = j;
     }
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Token-granular selection (papernotes 关键设计 2 read with q_i all query tokens of the
+// head): the pool of a head group is every (query token x, key block j) pair, L * N_b of
+// them, scored s = <q_x, Kbar_j> / sqrt(d).  The decision is that of
+// global_select_kernel, spread over many workgroups:
+//   token_scores_kernel  fp32 scores [G][L][N_b] on the fp32 matrix cores, and the head's
+//                        maximum as an atomic maximum of order keys;
+//   token_hist_kernel    one per 8-bit digit: (count, fixed-point mass) histograms of the
+//                        keys that match the digits decided so far, merged with global
+//                        atomics (integer sums, so their order does not matter);
+//   token_step_kernel    one thread per head group walks the merged histogram down from
+//                        the top digit;
+//   token_ties_*         only when the cut falls inside a run of equal keys: ranks of the
+//                        tied pairs in linear order x * N_b + j (per-chunk counts, scan);
+//   token_emit_kernel    the token mask [G][L][W] (W = ceil(N_b/32) words per token), the
+//                        union bitmap of every query block and the head's pair count;
+//   emit_lists_kernel    CSR / CSC of the union bitmap; token_stats_kernel the head stats.
+// Masses are held in 2^-36 units so that a head's total stays below 2^64 for pools of up
+// to 2^28 pairs.  Chunks are kTokChunk consecutive tokens (all their N_b pairs).
+constexpr double kTokMassUnit = 68719476736.0;   // 2^36
+constexpr int kTokChunk = 64;
+
+struct TokState {
+  unsigned long long R, above_mass, tie_mass, Z;
+  uint32_t mkey, prefix, above_cnt, tie_cnt, take, select_all, need_rank, nnz;
+};
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t token_mass(float s, float m) {
+  return uint64_t(double(expf(s - m)) * kTokMassUnit + 0.5);
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += size_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(64) void token_scores_kernel(Geom g, const T* __restrict__ q,
+                                                          const float* __restrict__ kp,
+                                                          float* __restrict__ scores,
+                                                          TokState* __restrict__ st,
+                                                          float scale) {
+  const int lane = threadIdx.x;
+  const int x0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const int grp = blockIdx.z;
+  const int half = lane >> 5;
+  const int rx = x0 + (lane & 31), rj = j0 + (lane & 31);
+  const int b = grp / g.Hh, h = grp - b * g.Hh;
+  const T* qrow = q + ((size_t(b) * g.L + min(rx, g.L - 1)) * g.Hh + h) * D + half * (D / 2);
+  const float* krow = kp + (size_t(grp) * g.Nb + min(rj, g.Nb - 1)) * D + half * (D / 2);
+  const bool qok = rx < g.L, kok = rj < g.Nb;
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  // lane half `half` feeds d in [half*D/2, (half+1)*D/2) for both operands
+#pragma unroll 4
+  for (int c = 0; c < D / 2; c += 4) {
+    float4 a;
+    if constexpr (sizeof(T) == 2) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(qrow + c);
+      a = make_float4(bf16_to_f32(w[0] & 0xffffu), bf16_to_f32(w[0] >> 16),
+                      bf16_to_f32(w[1] & 0xffffu), bf16_to_f32(w[1] >> 16));
+    } else {
+      a = *reinterpret_cast<const float4*>(qrow + c);
+    }
+    float4 bb = *reinterpret_cast<const float4*>(krow + c);
+    if (!qok) a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!kok) bb = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bb.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bb.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bb.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bb.w, acc, 0, 0, 0);
+  }
+  // acc[v]: token x0 + 8*(v/4) + 4*half + v%4, block j0 + lane%32
+  float mx = -INFINITY;
+  if (kok) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int x = x0 + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (x < g.L) {
+        const float sv = acc[v] * scale;
+        scores[(size_t(grp) * g.L + x) * g.Nb + rj] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) atomicMax(&st[grp].mkey, order_key(mx));
+}
+
+// Digit pass: histogram of digit (key >> shift) & 255 over the pairs whose higher digits
+// equal the prefix decided so far (pass 0: every pair).
+__global__ __launch_bounds__(256) void token_hist_kernel(Geom g, int shift,
+                                                         const float* __restrict__ scores,
+                                                         const TokState* __restrict__ st,
+                                                         uint32_t* __restrict__ hcnt,
+                                                         unsigned long long* __restrict__ hmass) {
+  __shared__ uint32_t cnt[256];
+  __shared__ unsigned long long mass[256];
+  const int grp = blockIdx.y;
+  const TokState S = st[grp];
+  if (S.select_all) return;
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  mass[tid] = 0;
+  __syncthreads();
+  const float m = key_to_float(S.mkey);
+  const uint32_t hi_mask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
+  const size_t N = size_t(g.L) * g.Nb;
+  const size_t begin = size_t(blockIdx.x) * kTokChunk * g.Nb;
+  const size_t end = min(N, begin + size_t(kTokChunk) * g.Nb);
+  const float* s = scores + size_t(grp) * N;
+  for (size_t base = begin; base < end; base += 256) {
+    const size_t idx = base + tid;
+    const bool in = idx < end;
+    const float sv = in ? s[idx] : -INFINITY;
+    const uint32_t key = order_key(sv);
+    const bool match = in && (key & hi_mask) == S.prefix;
+    const uint32_t dg = (key >> shift) & 0xffu;
+    histogram_add(cnt, mass, match, dg, match ? token_mass(sv, m) : 0ull);
+  }
+  __syncthreads();
+  if (cnt[tid]) {
+    atomicAdd(&hcnt[grp * 256 + tid], cnt[tid]);
+    atomicAdd(&hmass[grp * 256 + tid], mass[tid]);
+  }
+}
+
+// After digit pass `pass`: pick the digit where the running mass reaches the target, and
+// clear the histogram for the next pass.  One thread per head group.
+__global__ void token_step_kernel(int G, int pass, float tau, TokState* __restrict__ st,
+                                  uint32_t* __restrict__ hcnt,
+                                  unsigned long long* __restrict__ hmass) {
+  const int grp = blockIdx.x * blockDim.x + threadIdx.x;
+  if (grp >= G) return;
+  TokState& S = st[grp];
+  uint32_t* c = hcnt + grp * 256;
+  unsigned long long* ms = hmass + grp * 256;
+  if (pass == 0) {   // every pair matched: the histogram holds the whole pool
+    unsigned long long z = 0;
+    for (int d = 0; d < 256; ++d) z += ms[d];
+    S.Z = z;
+    S.R = (unsigned long long)ceil(double(tau) * double(z));
+    S.select_all = (tau >= 1.0f || S.R > z) ? 1u : 0u;
+    S.above_mass = 0;
+    S.above_cnt = 0;
+    S.prefix = 0;
+  }
+  if (!S.select_all) {
+    const int shift = 24 - 8 * pass;
+    unsigned long long acc = S.above_mass;
+    uint32_t n = S.above_cnt;
+    int dg = 255;
+    for (; dg >= 0; --dg) {
+      if (c[dg] > 0 && acc + ms[dg] >= S.R) break;
+      acc += ms[dg];
+      n += c[dg];
+    }
+    if (dg < 0) {
+      S.select_all = 1u;   // rounding kept the total below the target
+    } else {
+      S.above_mass = acc;
+      S.above_cnt = n;
+      S.prefix |= uint32_t(dg) << shift;
+      S.tie_cnt = c[dg];
+      S.tie_mass = ms[dg];
+    }
+    if (pass == 3 && !S.select_all) {
+      // all tied pairs share one score, hence one fixed-point mass
+      const unsigned long long e1 = S.tie_mass / S.tie_cnt;
+      const unsigned long long need = S.R - S.above_mass;
+      unsigned long long t = e1 ? (need + e1 - 1) / e1 : 1;
+      if (t < 1) t = 1;
+      if (t > S.tie_cnt) t = S.tie_cnt;
+      S.take = uint32_t(t);
+      S.need_rank = S.take < S.tie_cnt ? 1u : 0u;
+    }
+  }
+  for (int d = 0; d < 256; ++d) {
+    c[d] = 0;
+    ms[d] = 0;
+  }
+}
+
+// Tied pairs (key equal to the cut) per chunk, when only some of them are taken.
+__global__ __launch_bounds__(256) void token_ties_count_kernel(Geom g,
+                                                               const float* __restrict__ scores,
+                                                               const TokState* __restrict__ st,
+                                                               uint32_t* __restrict__ chunkcnt) {
+  __shared__ uint32_t red[4];
+  const int grp = blockIdx.y;
+  const TokState S = st[grp];
+  if (S.select_all || !S.need_rank) return;
+  const int tid = threadIdx.x;
+  const size_t N = size_t(g.L) * g.Nb;
+  const size_t begin = size_t(blockIdx.x) * kTokChunk * g.Nb;
+  const size_t end = min(N, begin + size_t(kTokChunk) * g.Nb);
+  const float* s = scores + size_t(grp) * N;
+  uint32_t n = 0;
+  for (size_t idx = begin + tid; idx < end; idx += 256) n += order_key(s[idx]) == S.prefix;
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+  if ((tid & 63) == 0) red[tid >> 6] = n;
+  __syncthreads();
+  if (tid == 0) chunkcnt[size_t(grp) * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+// Exclusive scan of the per-chunk tie counts of one head group (one workgroup each).
+__global__ __launch_bounds__(256) void token_ties_scan_kernel(int nchunks,
+                                                              const TokState* __restrict__ st,
+                                                              uint32_t* __restrict__ chunkcnt) {
+  __shared__ uint32_t part[256];
+  const int grp = blockIdx.x;
+  if (st[grp].select_all || !st[grp].need_rank) return;
+  const int tid = threadIdx.x;
+  uint32_t* c = chunkcnt + size_t(grp) * nchunks;
+  const int per = (nchunks + 255) / 256;
+  const int lo = min(nchunks, tid * per), hi = min(nchunks, lo + per);
+  uint32_t sum = 0;
+  for (int i = lo; i < hi; ++i) sum += c[i];
+  part[tid] = sum;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int i = 0; i < tid; ++i) off += part[i];
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t v = c[i];
+    c[i] = off;
+    off += v;
+  }
+}
+
+// Token mask, union bitmap and pair count.  Wave w of a chunk handles its tokens
+// kTokChunk/4 * w .. in order; each token's N_b pairs go 64 per ballot.
+__global__ __launch_bounds__(256) void token_emit_kernel(Geom g, const float* __restrict__ scores,
+                                                         TokState* __restrict__ st,
+                                                         const uint32_t* __restrict__ chunkoff,
+                                                         uint32_t* __restrict__ tokmask,
+                                                         uint32_t* __restrict__ qbits) {
+  constexpr int TPW = kTokChunk / 4;
+  __shared__ uint32_t wties[4];
+  const int grp = blockIdx.y;
+  const TokState S = st[grp];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool all = S.select_all != 0;
+  const uint32_t kstar = S.prefix;
+  const uint32_t take = all ? 0u : S.take;
+  const bool ranked = !all && S.need_rank;
+  const int Nb = g.Nb, W = (Nb + 31) / 32;
+  const size_t N = size_t(g.L) * Nb;
+  const float* s = scores + size_t(grp) * N;
+  const int x0 = blockIdx.x * kTokChunk + w * TPW;
+  const int x1 = min(g.L, x0 + TPW);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  uint32_t rank = 0;
+  if (ranked) {   // ties before this wave's tokens: earlier chunks, then earlier waves
+    uint32_t n = 0;
+    for (int x = x0; x < x1; ++x)
+      for (int jc = 0; jc < Nb; jc += 64) {
+        const int j = jc + lane;
+        n += __popcll(__ballot(j < Nb && order_key(s[size_t(x) * Nb + j]) == kstar));
+      }
+    if (lane == 0) wties[w] = n;
+    __syncthreads();
+    rank = chunkoff[size_t(grp) * gridDim.x + blockIdx.x];
+    for (int i = 0; i < w; ++i) rank += wties[i];
+  }
+  uint32_t nnz = 0;
+  for (int x = x0; x < x1; ++x) {
+    const int bx = token_block(g, x);
+    uint32_t* tm = tokmask + (size_t(grp) * g.L + x) * W;
+    uint32_t* qb = qbits + (size_t(grp) * Nb + bx) * W;
+    for (int jc = 0; jc < Nb; jc += 64) {
+      const int j = jc + lane;
+      const bool in = j < Nb;
+      const float sv = in ? s[size_t(x) * Nb + j] : -INFINITY;
+      const uint32_t key = order_key(sv);
+      const bool tie = in && !all && key == kstar;
+      const unsigned long long tb = __ballot(tie);
+      const uint32_t r = rank + uint32_t(__popcll(tb & lt));
+      rank += uint32_t(__popcll(tb));
+      const bool sel = in && (all || key > kstar || (tie && r < take) || j == bx);
+      const unsigned long long sb = __ballot(sel);
+      nnz += uint32_t(__popcll(sb));
+      const int wd = (jc >> 5) + (lane & 1);
+      const uint32_t word = (lane & 1) ? uint32_t(sb >> 32) : uint32_t(sb);
+      if (lane < 2 && wd < W) {
+        tm[wd] = word;
+        if (word) atomicOr(&qb[wd], word);
+      }
+    }
+  }
+  if (lane == 0 && nnz) atomicAdd(&st[grp].nnz, nnz);
+}
+
+__global__ void token_stats_kernel(int G, double npairs, const TokState* __restrict__ st,
+                                   float* __restrict__ head_stats) {
+  const int grp = blockIdx.x * blockDim.x + threadIdx.x;
+  if (grp >= G) return;
+  const TokState& S = st[grp];
+  float* hs = head_stats + size_t(grp) * 4;
+  if (S.select_all) {
+    hs[0] = float(npairs);
+    hs[2] = 1.0f;
+    hs[3] = 0.0f;
+  } else {
+    const double z = double(S.Z);
+    const unsigned long long e1 = S.tie_mass / S.tie_cnt;
+    hs[0] = float(S.above_cnt + S.take);
+    hs[2] = float(double(S.above_mass + e1 * S.take) / z);
+    hs[3] = float(double(e1) / z);
+  }
+  hs[1] = float(S.nnz);
 }
 
 template <bool TOPK>
@@ -625,6 +949,72 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
     return VMOBA_ERR_HIP;
   emit_lists_kernel<<<groups, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
       g.Nb, bitmap, rowstats, row_ptr, col_idx, col_ptr, row_idx, head_stats);
+  return launch_status();
+}
+
+// Workspace of the token-granular selection, in this order (256-byte aligned):
+// scores fp32 [G][L][N_b], TokState [G], histogram counts u32 [G][256], masses u64
+// [G][256], per-chunk tie counts u32 [G][chunks], union bitmap u32 [G][N_b][W].
+size_t token_select_ws(const Geom& g) {
+  const size_t G = size_t(g.B) * g.Hh;
+  const size_t W = (size_t(g.Nb) + 31) / 32;
+  const size_t chunks = (size_t(g.L) + kTokChunk - 1) / kTokChunk;
+  return align256(G * g.L * g.Nb * 4) + align256(G * sizeof(TokState)) + align256(G * 256 * 4) +
+         align256(G * 256 * 8) + align256(G * chunks * 4) + align256(G * g.Nb * W * 4);
+}
+
+int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, float tau,
+                         uint32_t* tokmask, int32_t* row_ptr, int32_t* col_idx,
+                         int32_t* col_ptr, int32_t* row_idx, float* head_stats, void* ws,
+                         void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = g.B * g.Hh;
+  const size_t W = (size_t(g.Nb) + 31) / 32;
+  const int chunks = (g.L + kTokChunk - 1) / kTokChunk;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  float* scores = reinterpret_cast<float*>(p);
+  p += align256(size_t(G) * g.L * g.Nb * 4);
+  TokState* state = reinterpret_cast<TokState*>(p);
+  p += align256(size_t(G) * sizeof(TokState));
+  uint32_t* hcnt = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(G) * 256 * 4);
+  unsigned long long* hmass = reinterpret_cast<unsigned long long*>(p);
+  p += align256(size_t(G) * 256 * 8);
+  uint32_t* chunkcnt = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(G) * chunks * 4);
+  uint32_t* qbits = reinterpret_cast<uint32_t*>(p);
+  // zero the state, the histograms and the union bitmap (a fill kernel, not a memset)
+  const size_t zero_words =
+      (reinterpret_cast<unsigned char*>(chunkcnt) - reinterpret_cast<unsigned char*>(state)) / 4;
+  fill_zero_kernel<<<1024, 256, 0, st>>>(reinterpret_cast<uint32_t*>(state), zero_words);
+  fill_zero_kernel<<<1024, 256, 0, st>>>(qbits, size_t(G) * g.Nb * W);
+  const float scale = 1.0f / sqrtf(float(g.D));
+  const dim3 sgrid((g.L + 31) / 32, (g.Nb + 31) / 32, G);
+  if (g.D == 128)
+    token_scores_kernel<128, uint16_t><<<sgrid, 64, 0, st>>>(
+        g, static_cast<const uint16_t*>(q), k_pool, scores, state, scale);
+  else
+    token_scores_kernel<64, uint16_t><<<sgrid, 64, 0, st>>>(
+        g, static_cast<const uint16_t*>(q), k_pool, scores, state, scale);
+  int stt = launch_status();
+  if (stt) return stt;
+  const dim3 cgrid(chunks, G);
+  const int sblocks = (G + 63) / 64;
+  for (int pass = 0; pass < 4; ++pass) {
+    token_hist_kernel<<<cgrid, 256, 0, st>>>(g, 24 - 8 * pass, scores, state, hcnt, hmass);
+    token_step_kernel<<<sblocks, 64, 0, st>>>(G, pass, tau, state, hcnt, hmass);
+  }
+  token_ties_count_kernel<<<cgrid, 256, 0, st>>>(g, scores, state, chunkcnt);
+  token_ties_scan_kernel<<<G, 256, 0, st>>>(chunks, state, chunkcnt);
+  token_emit_kernel<<<cgrid, 256, 0, st>>>(g, scores, state, chunkcnt, tokmask, qbits);
+  if ((stt = launch_status())) return stt;
+  const int max_lds = int(size_t(kMaxBlocks) * kMaxBlocks / 8);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
+    return VMOBA_ERR_HIP;
+  emit_lists_kernel<<<G, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
+      g.Nb, qbits, nullptr, row_ptr, col_idx, col_ptr, row_idx, nullptr);
+  token_stats_kernel<<<sblocks, 64, 0, st>>>(G, double(g.L) * g.Nb, state, head_stats);
   return launch_status();
 }
 

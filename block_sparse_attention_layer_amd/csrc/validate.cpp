@@ -87,6 +87,18 @@ int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
       // delta = rowsum(dO * O), fp32 [B][Hh][L]
       *bytes = align256(groups * size_t(g.L) * sizeof(float));
       return VMOBA_OK;
+    case VMOBA_OP_SELECT_TOKENS:
+      *bytes = token_select_ws(g);
+      return VMOBA_OK;
+    case VMOBA_OP_TOKEN_FWD:
+    case VMOBA_OP_TOKEN_BWD: {
+      // the token mask re-indexed by list position, u32 [B*Hh][L][ceil(N_b/32)]; the
+      // backward adds delta
+      const size_t words = (size_t(g.Nb) + 31) / 32;
+      *bytes = align256(groups * size_t(g.L) * words * 4);
+      if (op == VMOBA_OP_TOKEN_BWD) *bytes += align256(groups * size_t(g.L) * sizeof(float));
+      return VMOBA_OK;
+    }
     default:
       return VMOBA_ERR_OP;
   }

@@ -11,6 +11,8 @@
  *   vmoba_sparse_attn_fwd  attention restricted to the selected block pairs
  *   vmoba_sparse_attn_bwd  its gradient with the selection held constant
  *
+ * and the token-granular reading of the selection (vmoba_select_tokens, with
+ * vmoba_token_attn_fwd / _bwd under its per-token mask),
  * plus a dense flash-attention pair in the same library as the speed baseline.
  *
  * Conventions shared by every call
@@ -71,7 +73,10 @@ typedef enum {
   VMOBA_OP_SPARSE_FWD = 2,
   VMOBA_OP_SPARSE_BWD = 3,
   VMOBA_OP_DENSE_FWD = 4,
-  VMOBA_OP_DENSE_BWD = 5
+  VMOBA_OP_DENSE_BWD = 5,
+  VMOBA_OP_SELECT_TOKENS = 6,
+  VMOBA_OP_TOKEN_FWD = 7,
+  VMOBA_OP_TOKEN_BWD = 8
 } vmoba_op;
 
 /* Problem description (host struct, passed by pointer, read during the call only). */
@@ -191,6 +196,49 @@ int vmoba_sparse_attn_bwd_dq(const vmoba_problem* p, const void* q, const void* 
                              const void* v, const float* lse, const float* delta,
                              const void* dout, const int32_t* row_ptr,
                              const int32_t* col_idx, void* dq, void* stream);
+
+/* Token-granular selection: papernotes 关键设计 2 read with q_i all of the head's query
+ * tokens (s x d) instead of block means.  The pool of a head group is every (query token
+ * x, key block j) pair, L * N_b of them, s_xj = <q_x, k_pool_j>/sqrt(d) (fp32), normalised
+ * by a softmax over the whole pool; ranked descending (exact ties by ascending
+ * x*N_b + j), the shortest prefix whose normalised mass is >= tau is kept, and every token
+ * also keeps its own block.  q: [B][L][Hh][d] bf16 (fp32 problems are rejected with
+ * VMOBA_ERR_DTYPE); k_pool: fp32 [B][Hh][N_b][d] from vmoba_partition_pool.
+ * Outputs:
+ *   token_mask uint32 [G][L][W], W = ceil(N_b/32): bit (j & 31) of word (j >> 5) of token
+ *              x is set iff x attends to key block j (written in full);
+ *   row_ptr/col_idx, col_ptr/row_idx: CSR/CSC of the union over each query block's tokens
+ *              (query block i lists key block j iff some token of i selected j);
+ *   head_stats fp32 [G][4] = {k*, number of selected (token, block) pairs, prefix mass,
+ *              normalised score of the k*-th pair}.
+ * Needs L * N_b * G < 2^31 (VMOBA_ERR_OVERFLOW) and N_b <= 1024 (VMOBA_ERR_SHAPE).
+ * ws: vmoba_workspace_size(VMOBA_OP_SELECT_TOKENS) bytes (4 L N_b G bytes of scores and
+ * small tables). */
+int vmoba_select_tokens(const vmoba_problem* p, const void* q, const float* k_pool, float tau,
+                        uint32_t* token_mask, int32_t* row_ptr, int32_t* col_idx,
+                        int32_t* col_ptr, int32_t* row_idx, float* head_stats, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Attention under a token mask: query token x of query block i attends to the keys of the
+ * blocks j listed in CSR row i whose bit j is set in x's token_mask row (layout as
+ * vmoba_select_tokens).  A token with no such key gets O = 0 and lse = -inf.  bf16 only,
+ * blocks of at least 4 tokens (VMOBA_ERR_SHAPE otherwise).  ws:
+ * vmoba_workspace_size(VMOBA_OP_TOKEN_FWD) bytes (the mask re-indexed by list position,
+ * 4 G L ceil(N_b/32) bytes). */
+int vmoba_token_attn_fwd(const vmoba_problem* p, const void* q, const void* k, const void* v,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const uint32_t* token_mask, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Gradient of vmoba_token_attn_fwd with the selection held constant (formulas of
+ * vmoba_sparse_attn_bwd over the masked pairs).  The CSC must list the same block pairs as
+ * the CSR.  ws: vmoba_workspace_size(VMOBA_OP_TOKEN_BWD) bytes. */
+int vmoba_token_attn_bwd(const vmoba_problem* p, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout,
+                         const int32_t* row_ptr, const int32_t* col_idx,
+                         const int32_t* col_ptr, const int32_t* row_idx,
+                         const uint32_t* token_mask, void* dq, void* dk, void* dv, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Dense flash attention over all L x L pairs in natural token order (the baseline the
  * sparse layer replaces).  Shapes as the sparse calls; the block shape is ignored apart

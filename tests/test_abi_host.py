@@ -213,3 +213,36 @@ def test_select_mode_errors(L):
     assert L.vmoba_workspace_size(bp, 1, ctypes.byref(n)) == 0
     nb, groups = 8, p.batch * p.heads
     assert n.value >= groups * nb * nb * 4 + groups * nb * 4 + groups * nb * 12
+
+
+def test_token_call_errors(L):
+    """Token-granular calls: bf16 only, blocks of at least 4 tokens for the attention,
+    tau in (0, 1], null pointers and workspace checked before anything is enqueued."""
+    f32 = _prob()                                  # fp32 problem
+    bf = _prob(dtype=0, grad_dtype=1)
+    sel = lambda p, tau=0.25, ws=FAKE, n=1 << 30: L.vmoba_select_tokens(
+        ctypes.byref(p), FAKE, FAKE, tau, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, n, NULL)
+    assert sel(f32) == 5
+    for tau in (0.0, 1.5, float("nan")):
+        assert sel(bf, tau) == 4
+    assert sel(bf, 0.25, FAKE, 16) == 7
+    assert sel(bf, 0.25, NULL, 1 << 30) == 1
+    fwd = lambda p, ws=FAKE, n=1 << 30: L.vmoba_token_attn_fwd(
+        ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, n, NULL)
+    bwd = lambda p, ws=FAKE, n=1 << 30: L.vmoba_token_attn_bwd(
+        ctypes.byref(p), *([FAKE] * 14), ws, n, NULL)
+    tiny_blocks = _prob(dtype=0, grad_dtype=1, bt=1, bh=1, bw=2)   # 2 tokens per block
+    for call in (fwd, bwd):
+        assert call(f32) == 5
+        assert call(tiny_blocks) == 2
+        assert call(bf, FAKE, 16) == 7
+    # workspace: the list-position mask (and delta for the backward)
+    n = ctypes.c_size_t(0)
+    bp = ctypes.byref(bf)
+    G, Lt, nb = 2, 256, 8
+    assert L.vmoba_workspace_size(bp, OPS["token_fwd"], ctypes.byref(n)) == 0
+    assert n.value >= G * Lt * 4
+    assert L.vmoba_workspace_size(bp, OPS["token_bwd"], ctypes.byref(n)) == 0
+    assert n.value >= G * Lt * 4 + G * Lt * 4
+    assert L.vmoba_workspace_size(bp, OPS["select_tokens"], ctypes.byref(n)) == 0
+    assert n.value >= G * Lt * nb * 4
