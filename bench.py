@@ -40,6 +40,8 @@ def parse():
                     choices=["threshold_global", "topk_global", "threshold_local", "topk_local"],
                     help="selection strategy (the method's is threshold_global)")
     ap.add_argument("--topk", type=int, default=None, help="k of the top-k strategies")
+    ap.add_argument("--granularity", default="block", choices=["block", "token"],
+                    help="token: the token-granular query pool (prints its own line)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every bf16 workload, layer and tau (one JSON line each)")
     ap.add_argument("--sweep-workloads", default=None,
@@ -226,6 +228,75 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
                 dense=dense, cpu=cpu)
 
 
+def run_tokens(workload, layer, tau, steps, warmup):
+    """Time the token-granular path of one layer (pool, token selection, forward under the
+    token mask, backward) and print one JSON line."""
+    import torch
+    from synthetic import CONFIGS, make_layer_inputs
+    import block_sparse_attention_layer_amd as vm
+
+    cfg = CONFIGS[workload]
+    spec = cfg["layers"][layer]
+    if tau is None:
+        tau = 0.25 if 0.25 in cfg["taus"] else cfg["taus"][0]
+    dev = torch.device("cuda:0")
+    inp = make_layer_inputs(workload, layer, backward=True)
+    p = vm.Problem(cfg["batch"], cfg["heads"], cfg["head_dim"], cfg["T"], cfg["H"], cfg["W"],
+                   spec.layer_idx, tuple(spec.block), torch.bfloat16, torch.bfloat16)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    nb = vm.vmoba_num_blocks(p)
+    S = p.L // nb
+    d = p.head_dim
+    names = ["pool", "select_tokens", "fwd", "bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        _, kp = vm.vmoba_partition_pool(p, q, k)
+        mark(1)
+        sel = vm.vmoba_select_tokens(p, q, kp, tau)
+        mark(2)
+        o, lse = vm.vmoba_token_attn_fwd(p, q, k, v, sel.row_ptr, sel.col_idx, sel.token_mask)
+        mark(3)
+        vm.vmoba_token_attn_bwd(p, q, k, v, o, lse, do, sel.row_ptr, sel.col_idx, sel.col_ptr,
+                                sel.row_idx, sel.token_mask)
+        mark(4)
+        return sel
+
+    for _ in range(warmup):
+        sel = step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sel = step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    st = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    tok_pairs = float(sel.head_stats[:, 1].double().sum().item())     # (token, block) pairs
+    union_pairs = float(sel.row_ptr[:, -1].double().sum().item())      # listed block pairs
+    pairs = tok_pairs * S                        # (query token, key token) pairs attended
+    walked = union_pairs * S * S                 # pairs the kernels walk (masked ones too)
+    line = {
+        "metric": "VMoBA token-granular pool: attn fwd+bwd TFLOP/s at 55K tokens",
+        "value": round(12.0 * d * pairs / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{workload} layer {layer} (blocks {tuple(spec.block)}, "
+                               f"{nb} of {S}), tau {tau}, token-granular query pool"},
+        "stages_ms": {n: round(st[n], 4) for n in names},
+        "selected_token_pairs": pairs, "walked_token_pairs": walked,
+        "kept_fraction_of_walked": round(pairs / walked, 4),
+        "token_pair_density": round(pairs / (p.groups * float(p.L) ** 2), 5),
+        "fwd_tflops_walked": round(4.0 * d * walked / (st["fwd"] * 1e-3) / 1e12, 2),
+        "select_gbs": round(p.groups * float(p.L) * nb * 4 * 6 / (st["select_tokens"] * 1e-3)
+                            / 1e9, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def describe(workload, r):
     p, spec = r["p"], r["spec"]
     sel = ("" if r.get("mode", "threshold_global") == "threshold_global"
@@ -271,6 +342,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.granularity == "token":
+        run_tokens(args.workload, args.layer, args.tau, args.steps, args.warmup)
         return
 
     r = run_config(args.workload, args.layer, args.tau, args.steps, args.warmup,

@@ -129,3 +129,70 @@ def test_selection_modes_full_size(layer):
         print(f"  {mode} tau={tau} k={k} density={gm.mean():.4f} mismatches={bad} "
               f"exempt={exempt}", flush=True)
         assert bad == 0
+
+
+@pytest.mark.parametrize("name,li", [("l3d_55k", 0), ("blocks_55k", 2)],
+                         ids=["l3d_55k-L0", "blocks_55k-L2"])
+def test_token_granular_full_size(name, li):
+    """Token-granular pool at full length on two heads (heads are independent problems):
+    the token mask against the oracle's (cutoff window 1e-4 relative), then the attention
+    on the oracle's mask: sampled rows (O, LSE, dQ) and the two sum identities."""
+    from oracle import tokens as otok
+    from block_sparse_attention_layer_amd import (vmoba_partition_pool, vmoba_select_tokens,
+                                                  vmoba_token_attn_bwd, vmoba_token_attn_fwd)
+    from test_gpu_tokens import bits_to_bool, bool_to_bits
+    cfg = CONFIGS[name]
+    spec = cfg["layers"][li]
+    print(f"[full-size token pool {name} layer {li}] generating inputs", flush=True)
+    full = make_layer_inputs(name, li, backward=True)
+    heads = [0, cfg["heads"] - 1]
+    inp = {x: full[x][:, :, heads].contiguous() for x in ("q", "k", "v", "do")}
+    del full
+    p = Problem(cfg["batch"], len(heads), cfg["head_dim"], cfg["T"], cfg["H"], cfg["W"],
+                spec.layer_idx, tuple(spec.block), torch.bfloat16, torch.float32)
+    mem = oracle.block_members(p.T, p.H, p.W, p.block)
+    blk = oracle.block_of_token(mem, p.L)
+    nb = mem.shape[0]
+    qn, kn = to_np(inp["q"]), to_np(inp["k"])
+    mask, shat, stats = otok.select_tokens_all_heads(qn, oracle.block_means(kn, mem), 0.25, blk)
+    del kn
+    print(f"  oracle done: pool {p.L}x{nb}, k* {[s['k'] for s in stats]}", flush=True)
+    d = {x: inp[x].to(DEV) for x in ("q", "k", "v", "do")}
+    _, kp = vmoba_partition_pool(p, d["q"], d["k"])
+    sel = vmoba_select_tokens(p, d["q"], kp, 0.25)
+    torch.cuda.synchronize()
+    gm = bits_to_bool(sel.token_mask, nb)
+    bad = exempt = 0
+    for h in range(p.heads):
+        v = stats[h]["v"]
+        diff = gm[h] != mask[0, h]
+        near = np.abs(shat[0, h] - v) <= 1e-4 * v
+        bad += int((diff & ~near).sum())
+        exempt += int((diff & near).sum())
+    print(f"  mask mismatches {bad} exempt {exempt} density {gm.mean():.4f}", flush=True)
+    assert bad == 0
+    del shat
+    union = otok.union_block_mask(mask, mem)
+    rp, ci, cp, ri = csr_to_device(union, DEV)
+    bits = bool_to_bits(mask[0]).to(DEV)
+    o, lse = vmoba_token_attn_fwd(p, d["q"], d["k"], d["v"], rp, ci, bits)
+    dq, dk, dv = vmoba_token_attn_bwd(p, d["q"], d["k"], d["v"], o, lse, d["do"], rp, ci, cp,
+                                      ri, bits)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    q, k, v, do = (inp[x].float().numpy() for x in ("q", "k", "v", "do"))
+    on, ln, dqn = o.float().cpu().numpy(), lse.cpu().numpy(), dq.cpu().numpy()
+    for h in range(p.heads):
+        rows = np.sort(rng.choice(p.L, 48, replace=False))
+        got = otok.sampled_token_rows(q, k, v, do, mask, mem, blk, 0, h, rows)
+        for x, r in zip(rows, got):
+            assert np.abs(on[0, x, h] - r["o"]).max() <= TOL
+            assert abs(ln[0, h, x] - r["lse"]) <= TOL
+            assert np.abs(dqn[0, x, h] - r["dq"]).max() <= TOL
+    # sum_y dV_y = sum_x dO_x and sum_y dK_y = 0 (fp64 sums of the fp32 gradients)
+    dvs = dv.double().sum(dim=1).cpu().numpy()
+    dos = inp["do"].double().sum(dim=1).numpy()
+    dks = dk.double().sum(dim=1).cpu().numpy()
+    scale = np.abs(dos).max()
+    assert np.abs(dvs - dos).max() <= 1e-3 * scale
+    assert np.abs(dks).max() <= 1e-3 * max(1.0, np.abs(dk.double().cpu().numpy()).sum(axis=1).max())
