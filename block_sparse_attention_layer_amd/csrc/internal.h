@@ -31,6 +31,9 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
                   int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
                   void* stream);
 
+// Workspace sizes of the selection calls (select.hip).
+size_t select_ws(const Geom& g);
+
 // Token-granular selection (select.hip); token_select_ws is its workspace size.
 size_t token_select_ws(const Geom& g);
 int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, float tau,

@@ -1,33 +1,36 @@
-// Global block selection with the cumulative-mass threshold (papernotes 关键设计 2 and 3;
-// paperlayer §3.3-§3.4).
+// Block selection with the cumulative-mass threshold (papernotes 关键设计 2 and 3;
+// paperlayer §3.3-§3.4) and the other strategies of the ablation.
 //
-// Stage 1, block_scores_kernel: s_ij = <Qbar_i, Kbar_j> / sqrt(d) for one 32 x 32 tile of
-// one head group per wave, on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), so the
-// products and sums keep fp32 precision; the selection compares masses near tau.
+// Scores: block_scores_kernel computes s_ij = <Qbar_i, Kbar_j> / sqrt(d) for one 32 x 32
+// tile of one head group per wave, on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), so
+// the products and sums keep fp32 precision; the selection compares masses near tau.
 //
-// Stage 2, threshold_select_kernel: one 1024-thread workgroup per head group.
-//   1. m = max s; each pair's mass e = exp(s - m) is held as a 64-bit fixed-point integer
-//      (2^44 units), so every mass sum is exact and independent of summation order.
+// Global strategies (threshold + global, the method's; top-k + global): the N_b x N_b
+// pool of a head group goes through the pool selection further down, spread over many
+// workgroups:
+//   1. m = max s; each pair's mass e = exp(s - m) is held as a 64-bit fixed-point integer,
+//      so every mass sum is exact and independent of summation order.
 //   2. The cutoff pair is found without sorting: the fp32 scores are mapped to
 //      order-preserving 32-bit keys, and four 8-bit radix passes build per-digit
 //      (count, mass) histograms of the still-undecided keys, walking down from the
-//      largest digit until the running mass reaches ceil(tau * sum e).  What remains is
-//      the key of the k*-th pair; exact ties at that key are taken in ascending linear
-//      index i*N_b + j, as many as the threshold needs.
-//   3. Compaction in linear order marks the prefix plus the diagonal in an LDS bitmap
-//      (wave ballots, one 64-bit word per wave), then row and column counts, an
-//      exclusive scan and an ascending walk per row / column emit CSR and CSC.
-//   With TOPK the same walk counts pairs instead of mass: the cutoff is the key of the
-//   k-th pair (top-k + global, one of the strategies of the ablation, paperlayer §4.4).
+//      largest digit until the running mass reaches ceil(tau * sum e) (top-k: the
+//      running count reaches k).  What remains is the key of the k*-th pair; exact ties at
+//      that key are taken in ascending linear index i*N_b + j, as many as needed.
+//   3. The prefix plus the diagonal go to a row bitmap (wave ballots in linear order),
+//      and emit_lists_kernel turns the bitmap into CSR and CSC (row and column counts, an
+//      exclusive scan, an ascending walk per row / column).
+// The same passes select over the token-granular pool (query tokens x key blocks).
 //
 // Local strategies (threshold + local, top-k + local): every query block's row of N_b
 // scores is its own pool, normalised by a softmax over the row.  select_local_kernel
 // gives each row one wave; a pair is kept iff the fixed-point mass (threshold) or the
 // number (top-k) of the row's pairs that precede it in the order (higher score, or the
 // same score at a lower key index) is below the target.  Each lane counts that for its
-// pairs against the whole row staged in LDS.  The rows go to a bitmap, and
-// emit_lists_kernel turns the bitmap into CSR and CSC as above.
+// pairs against the whole row staged in LDS.  The rows go to the bitmap, and
+// emit_lists_kernel turns it into CSR and CSC as above.
 #include <math.h>
+
+#include <algorithm>
 
 #include "device_common.h"
 
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(int Nb, const float* _
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr double kMassUnit = 17592186044416.0;  // 2^44
+constexpr double kMassUnit = 17592186044416.0;  // 2^44 (a local pool of <= 1024 pairs)
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t b = __float_as_uint(s);
@@ -88,16 +91,10 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float m) {
   return uint64_t(double(e) * kMassUnit + 0.5);
 }
 
+// Shared memory of emit_lists_kernel.
 struct SelShared {
-  uint32_t cnt[256];
-  unsigned long long mass[256];
   float redf[kSelWaves];
-  unsigned long long redu[kSelWaves];
   uint32_t redi[kSelWaves];
-  // selection state (written by thread 0)
-  float m;
-  unsigned long long Z, R, above_mass, tie_mass;
-  uint32_t prefix, above_cnt, tie_cnt, take_ties, select_all, tie_seen;
   int32_t row_cnt[kMaxBlocks];
   int32_t col_cnt[kMaxBlocks];
 };
@@ -130,33 +127,6 @@ __device__ __forceinline__ void histogram_add(uint32_t* cnt, unsigned long long*
   }
 }
 
-__device__ __forceinline__ void histogram_add(SelShared& sh, bool match, uint32_t dg,
-                                              unsigned long long mass) {
-  histogram_add(sh.cnt, sh.mass, match, dg, mass);
-}
-
-__device__ float block_max(float v, SelShared& sh) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh.redf[w] = v;
-  __syncthreads();
-  float r = sh.redf[0];
-  for (int i = 1; i < kSelWaves; ++i) r = fmaxf(r, sh.redf[i]);
-  __syncthreads();
-  return r;
-}
-
-__device__ unsigned long long block_sum_u64(unsigned long long v, SelShared& sh) {
-  v = wave_sum_u64(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh.redu[w] = v;
-  __syncthreads();
-  unsigned long long r = 0;
-  for (int i = 0; i < kSelWaves; ++i) r += sh.redu[i];
-  __syncthreads();
-  return r;
-}
-
 // Exclusive scan of one int per thread (thread order); returns the block total in *total.
 __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -176,200 +146,6 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   __syncthreads();
   *total = tot;
   return off + x - v;
-}
-
-template <bool TOPK>
-__global__ __launch_bounds__(kSelThreads) void global_select_kernel(
-    int Nb, float tau, int topk, const float* __restrict__ scores, int32_t* __restrict__ row_ptr,
-    int32_t* __restrict__ col_idx, int32_t* __restrict__ col_ptr,
-    int32_t* __restrict__ row_idx, float* __restrict__ head_stats,
-    float* __restrict__ norm_scores) {
-  __shared__ SelShared sh;
-  extern __shared__ uint32_t bits[];  // N_b*N_b-bit pair bitmap, padded to 64-bit words
-  const int grp = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int N = Nb * Nb;
-  const float* s = scores + size_t(grp) * N;
-
-  // 1. max and total fixed-point mass
-  float mx = -INFINITY;
-  for (int idx = tid; idx < N; idx += kSelThreads) mx = fmaxf(mx, s[idx]);
-  mx = block_max(mx, sh);
-  unsigned long long z = 0;
-  for (int idx = tid; idx < N; idx += kSelThreads) z += fixed_mass(s[idx], mx);
-  z = block_sum_u64(z, sh);
-  if (tid == 0) {
-    sh.m = mx;
-    sh.Z = z;
-    if constexpr (TOPK) {
-      sh.R = (unsigned long long)topk;   // a count of pairs
-      sh.select_all = topk >= N ? 1u : 0u;
-    } else {
-      const double r = ceil(double(tau) * double(z));
-      sh.R = (unsigned long long)r;
-      sh.select_all = (tau >= 1.0f || sh.R > z) ? 1u : 0u;
-    }
-    sh.prefix = 0;
-    sh.above_cnt = 0;
-    sh.above_mass = 0;
-  }
-  __syncthreads();
-
-  // 2. four radix passes over the order keys, most significant digit first
-  if (!sh.select_all) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-      for (int d = tid; d < 256; d += kSelThreads) {
-        sh.cnt[d] = 0;
-        sh.mass[d] = 0;
-      }
-      __syncthreads();
-      const uint32_t prefix = sh.prefix;
-      for (int base = 0; base < N; base += kSelThreads) {
-        const int idx = base + tid;
-        const float sv = idx < N ? s[idx] : -INFINITY;
-        const uint32_t key = order_key(sv);
-        const bool match = idx < N && (key & hi_mask) == prefix;
-        const uint32_t dg = (key >> shift) & 0xffu;
-        const unsigned long long ms = match ? fixed_mass(sv, mx) : 0ull;
-        histogram_add(sh, match, dg, ms);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        unsigned long long acc = sh.above_mass;
-        uint32_t cnt = sh.above_cnt;
-        int dg = 255;
-        for (; dg >= 0; --dg) {
-          const bool reach = TOPK ? cnt + sh.cnt[dg] >= sh.R : acc + sh.mass[dg] >= sh.R;
-          if (reach && sh.cnt[dg] > 0) break;
-          acc += sh.mass[dg];
-          cnt += sh.cnt[dg];
-        }
-        if (dg < 0) {
-          sh.select_all = 1u;  // rounding kept the total below the target
-        } else {
-          sh.above_mass = acc;
-          sh.above_cnt = cnt;
-          sh.prefix = prefix | (uint32_t(dg) << shift);
-          sh.tie_cnt = sh.cnt[dg];
-          sh.tie_mass = sh.mass[dg];
-        }
-      }
-      __syncthreads();
-      if (sh.select_all) break;
-    }
-  }
-  if (tid == 0 && !sh.select_all) {
-    // all tied pairs share one score, hence one fixed-point mass
-    const unsigned long long e1 = sh.tie_mass / sh.tie_cnt;
-    const unsigned long long need = sh.R - (TOPK ? sh.above_cnt : sh.above_mass);
-    unsigned long long t = TOPK ? need : (e1 ? (need + e1 - 1) / e1 : 1);
-    if (t < 1) t = 1;
-    if (t > sh.tie_cnt) t = sh.tie_cnt;
-    sh.take_ties = uint32_t(t);
-  }
-  if (tid == 0) sh.tie_seen = 0;
-  __syncthreads();
-
-  // 3. compaction in linear order into the LDS bitmap
-  const bool all = sh.select_all != 0;
-  const uint32_t kstar = sh.prefix;
-  const uint32_t take = all ? 0u : sh.take_ties;
-  const int lane = tid & 63, w = tid >> 6;
-  const float inv_z = float(kMassUnit / double(sh.Z));
-  for (int base = 0; base < N; base += kSelThreads) {
-    const int idx = base + tid;
-    const bool in = idx < N;
-    const float sv = in ? s[idx] : -INFINITY;
-    const uint32_t key = order_key(sv);
-    const bool tie = in && !all && key == kstar;
-    // rank of this tie among ties in linear order
-    const unsigned long long tmask = __ballot(tie);
-    const int before_in_wave = __popcll(tmask & ((1ull << lane) - 1ull));
-    if (lane == 0) sh.redi[w] = uint32_t(__popcll(tmask));
-    __syncthreads();
-    int before = int(sh.tie_seen);
-    int total = 0;
-    for (int i = 0; i < kSelWaves; ++i) {
-      if (i < w) before += int(sh.redi[i]);
-      total += int(sh.redi[i]);
-    }
-    const int rank = before + before_in_wave;
-    const int i_row = in ? idx / Nb : 0;
-    const bool diag = in && (idx - i_row * Nb) == i_row;
-    const bool sel = in && (all || key > kstar || (tie && uint32_t(rank) < take) || diag);
-    const unsigned long long smask = __ballot(sel);
-    if (lane == 0) {
-      const int word = (base >> 5) + 2 * w;
-      bits[word] = uint32_t(smask);
-      bits[word + 1] = uint32_t(smask >> 32);
-    }
-    if (norm_scores && in) norm_scores[size_t(grp) * N + idx] = expf(sv - sh.m) * inv_z;
-    __syncthreads();
-    if (tid == 0) sh.tie_seen += uint32_t(total);
-    __syncthreads();
-  }
-
-  // 4. CSR / CSC from the bitmap
-  for (int i = tid; i < Nb; i += kSelThreads) {
-    int rc = 0, cc = 0;
-    for (int j = 0; j < Nb; ++j) {
-      const int ir = i * Nb + j, ic = j * Nb + i;
-      rc += (bits[ir >> 5] >> (ir & 31)) & 1u;
-      cc += (bits[ic >> 5] >> (ic & 31)) & 1u;
-    }
-    sh.row_cnt[i] = rc;
-    sh.col_cnt[i] = cc;
-  }
-  __syncthreads();
-  int32_t* rp = row_ptr + size_t(grp) * (Nb + 1);
-  int32_t* cp = col_ptr + size_t(grp) * (Nb + 1);
-  // Nb <= kMaxBlocks = kSelThreads: one entry per thread
-  {
-    const int rc = tid < Nb ? sh.row_cnt[tid] : 0;
-    const int cc = tid < Nb ? sh.col_cnt[tid] : 0;
-    int rtot = 0, ctot = 0;
-    const int roff = block_excl_scan(rc, sh, &rtot);
-    const int coff = block_excl_scan(cc, sh, &ctot);
-    __syncthreads();
-    if (tid < Nb) {
-      sh.row_cnt[tid] = roff;
-      sh.col_cnt[tid] = coff;
-      rp[tid] = roff;
-      cp[tid] = coff;
-    }
-    if (tid == 0) {
-      rp[Nb] = rtot;
-      cp[Nb] = ctot;
-      if (head_stats) {
-        float* hs = head_stats + size_t(grp) * 4;
-        const double zz = double(sh.Z);
-        if (all) {
-          hs[0] = float(N);
-          hs[2] = 1.0f;
-          hs[3] = 0.0f;
-        } else {
-          const unsigned long long e1 = sh.tie_mass / sh.tie_cnt;
-          hs[0] = float(sh.above_cnt + sh.take_ties);
-          hs[2] = float(double(sh.above_mass + e1 * sh.take_ties) / zz);
-          hs[3] = float(double(e1) / zz);
-        }
-        hs[1] = float(rtot);
-      }
-    }
-  }
-  __syncthreads();
-  int32_t* ci = col_idx + size_t(grp) * N;
-  int32_t* ri = row_idx + size_t(grp) * N;
-  for (int i = tid; i < Nb; i += kSelThreads) {
-    int pr = sh.row_cnt[i], pc = sh.col_cnt[i];
-    for (int j = 0; j < Nb; ++j) {
-      const int ir = i * Nb + j, ic = j * Nb + i;
-      if ((bits[ir >> 5] >> (ir & 31)) & 1u) ci[pr++] = j;
-      if ((bits[ic >> 5] >> (ic & 31)) & 1u) ri[pc++] = j;
-    }
-  }
 }
 
 // One wave per query-block row; U = ceil(N_b / 64) pairs per lane.  rowstats[G][N_b][3] =
@@ -565,28 +341,28 @@ __global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// Token-granular selection (papernotes 关键设计 2 read with q_i all query tokens of the
-// head): the pool of a head group is every (query token x, key block j) pair, L * N_b of
-// them, scored s = <q_x, Kbar_j> / sqrt(d).  The decision is that of
-// global_select_kernel, spread over many workgroups:
-//   token_scores_kernel  fp32 scores [G][L][N_b] on the fp32 matrix cores, and the head's
-//                        maximum as an atomic maximum of order keys;
-//   token_hist_kernel    one per 8-bit digit: (count, fixed-point mass) histograms of the
-//                        keys that match the digits decided so far, merged with global
-//                        atomics (integer sums, so their order does not matter);
-//   token_step_kernel    one thread per head group walks the merged histogram down from
-//                        the top digit;
-//   token_ties_*         only when the cut falls inside a run of equal keys: ranks of the
-//                        tied pairs in linear order x * N_b + j (per-chunk counts, scan);
-//   token_emit_kernel    the token mask [G][L][W] (W = ceil(N_b/32) words per token), the
-//                        union bitmap of every query block and the head's pair count;
-//   emit_lists_kernel    CSR / CSC of the union bitmap; token_stats_kernel the head stats.
-// Masses are held in 2^-36 units so that a head's total stays below 2^64 for pools of up
-// to 2^28 pairs.  Chunks are kTokChunk consecutive tokens (all their N_b pairs).
-constexpr double kTokMassUnit = 68719476736.0;   // 2^36
-constexpr int kTokChunk = 64;
-
-struct TokState {
+// Pool selection over many workgroups.  A head group's pool is `rows` x N_b scores in
+// row-major order (linear index row * N_b + j): the N_b x N_b block pairs of the global
+// strategies (rows = query blocks, forced pair (i, i)), or the L x N_b (query token, key
+// block) pairs of the token-granular reading of papernotes 关键设计 2 (rows = tokens, forced
+// pair (x, block(x))).  The decision is the threshold (or top-k) rule of the single-head
+// description above:
+//   scores             block_scores_kernel / token_scores_kernel, which also record the
+//                      head's maximum as an atomic maximum of order keys;
+//   pool_hist_kernel   one per 8-bit digit: (count, fixed-point mass) histograms of the keys
+//                      that match the digits decided so far, merged with global atomics
+//                      (integer sums, so the order of the atomics does not matter);
+//   pool_step_kernel   one thread per head group walks the merged histogram down from the
+//                      top digit to where the running mass (or count) reaches the target;
+//   pool_ties_*        only when the cut falls inside a run of equal keys: the ranks of the
+//                      tied pairs in linear order (per-chunk counts, then a scan);
+//   pool_emit_kernel   the row bitmap [G][rows][W] (W = ceil(N_b/32) words per row) and,
+//                      for token rows, the union bitmap of every query block;
+//   emit_lists_kernel  CSR / CSC of the block bitmap; pool_stats_kernel the head stats.
+// A chunk is `rpc` consecutive rows (a multiple of 4: one quarter per wave).  Masses are
+// integers in units of 2^-unit_log2 of the largest one, with unit_log2 chosen per pool so
+// that a head's total stays below 2^63.
+struct PoolState {
   unsigned long long R, above_mass, tie_mass, Z;
   uint32_t mkey, prefix, above_cnt, tie_cnt, take, select_all, need_rank, nnz;
 };
@@ -595,8 +371,15 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__device__ __forceinline__ uint64_t token_mass(float s, float m) {
-  return uint64_t(double(expf(s - m)) * kTokMassUnit + 0.5);
+__device__ __forceinline__ uint64_t pool_mass(float s, float m, double unit) {
+  return uint64_t(double(expf(s - m)) * unit + 0.5);
+}
+
+// largest power-of-two unit with npairs * unit < 2^63 (at most 2^44)
+inline double pool_unit(double npairs) {
+  int b = 0;
+  while (b < 62 && double(uint64_t(1) << b) < npairs) ++b;
+  return ldexp(1.0, std::min(44, 62 - b));
 }
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
@@ -605,11 +388,21 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
     p[i] = 0u;
 }
 
+__global__ void pool_max_kernel(int N, const float* __restrict__ scores,
+                                PoolState* __restrict__ st) {
+  const int grp = blockIdx.y;
+  float mx = -INFINITY;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256)
+    mx = fmaxf(mx, scores[size_t(grp) * N + i]);
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) atomicMax(&st[grp].mkey, order_key(mx));
+}
+
 template <int D, typename T>
 __global__ __launch_bounds__(64) void token_scores_kernel(Geom g, const T* __restrict__ q,
                                                           const float* __restrict__ kp,
                                                           float* __restrict__ scores,
-                                                          TokState* __restrict__ st,
+                                                          PoolState* __restrict__ st,
                                                           float scale) {
   const int lane = threadIdx.x;
   const int x0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
@@ -661,15 +454,16 @@ __global__ __launch_bounds__(64) void token_scores_kernel(Geom g, const T* __res
 
 // Digit pass: histogram of digit (key >> shift) & 255 over the pairs whose higher digits
 // equal the prefix decided so far (pass 0: every pair).
-__global__ __launch_bounds__(256) void token_hist_kernel(Geom g, int shift,
-                                                         const float* __restrict__ scores,
-                                                         const TokState* __restrict__ st,
-                                                         uint32_t* __restrict__ hcnt,
-                                                         unsigned long long* __restrict__ hmass) {
+__global__ __launch_bounds__(256) void pool_hist_kernel(int rows, int Nb, int rpc, int shift,
+                                                        double unit,
+                                                        const float* __restrict__ scores,
+                                                        const PoolState* __restrict__ st,
+                                                        uint32_t* __restrict__ hcnt,
+                                                        unsigned long long* __restrict__ hmass) {
   __shared__ uint32_t cnt[256];
   __shared__ unsigned long long mass[256];
   const int grp = blockIdx.y;
-  const TokState S = st[grp];
+  const PoolState S = st[grp];
   if (S.select_all) return;
   const int tid = threadIdx.x;
   cnt[tid] = 0;
@@ -677,9 +471,9 @@ __global__ __launch_bounds__(256) void token_hist_kernel(Geom g, int shift,
   __syncthreads();
   const float m = key_to_float(S.mkey);
   const uint32_t hi_mask = shift == 24 ? 0u : (0xffffffffu << (shift + 8));
-  const size_t N = size_t(g.L) * g.Nb;
-  const size_t begin = size_t(blockIdx.x) * kTokChunk * g.Nb;
-  const size_t end = min(N, begin + size_t(kTokChunk) * g.Nb);
+  const size_t N = size_t(rows) * Nb;
+  const size_t begin = size_t(blockIdx.x) * rpc * Nb;
+  const size_t end = min(N, begin + size_t(rpc) * Nb);
   const float* s = scores + size_t(grp) * N;
   for (size_t base = begin; base < end; base += 256) {
     const size_t idx = base + tid;
@@ -688,7 +482,7 @@ __global__ __launch_bounds__(256) void token_hist_kernel(Geom g, int shift,
     const uint32_t key = order_key(sv);
     const bool match = in && (key & hi_mask) == S.prefix;
     const uint32_t dg = (key >> shift) & 0xffu;
-    histogram_add(cnt, mass, match, dg, match ? token_mass(sv, m) : 0ull);
+    histogram_add(cnt, mass, match, dg, match ? pool_mass(sv, m, unit) : 0ull);
   }
   __syncthreads();
   if (cnt[tid]) {
@@ -697,22 +491,28 @@ __global__ __launch_bounds__(256) void token_hist_kernel(Geom g, int shift,
   }
 }
 
-// After digit pass `pass`: pick the digit where the running mass reaches the target, and
-// clear the histogram for the next pass.  One thread per head group.
-__global__ void token_step_kernel(int G, int pass, float tau, TokState* __restrict__ st,
-                                  uint32_t* __restrict__ hcnt,
-                                  unsigned long long* __restrict__ hmass) {
+// After digit pass `pass`: pick the digit where the running mass (topk > 0: count)
+// reaches the target, and clear the histogram for the next pass.  One thread per group.
+__global__ void pool_step_kernel(int G, int pass, float tau, int topk, double npairs,
+                                 PoolState* __restrict__ st, uint32_t* __restrict__ hcnt,
+                                 unsigned long long* __restrict__ hmass) {
   const int grp = blockIdx.x * blockDim.x + threadIdx.x;
   if (grp >= G) return;
-  TokState& S = st[grp];
+  PoolState& S = st[grp];
   uint32_t* c = hcnt + grp * 256;
   unsigned long long* ms = hmass + grp * 256;
+  const bool count = topk > 0;
   if (pass == 0) {   // every pair matched: the histogram holds the whole pool
     unsigned long long z = 0;
     for (int d = 0; d < 256; ++d) z += ms[d];
     S.Z = z;
-    S.R = (unsigned long long)ceil(double(tau) * double(z));
-    S.select_all = (tau >= 1.0f || S.R > z) ? 1u : 0u;
+    if (count) {
+      S.R = (unsigned long long)topk;
+      S.select_all = double(topk) >= npairs ? 1u : 0u;
+    } else {
+      S.R = (unsigned long long)ceil(double(tau) * double(z));
+      S.select_all = (tau >= 1.0f || S.R > z) ? 1u : 0u;
+    }
     S.above_mass = 0;
     S.above_cnt = 0;
     S.prefix = 0;
@@ -723,7 +523,8 @@ __global__ void token_step_kernel(int G, int pass, float tau, TokState* __restri
     uint32_t n = S.above_cnt;
     int dg = 255;
     for (; dg >= 0; --dg) {
-      if (c[dg] > 0 && acc + ms[dg] >= S.R) break;
+      const bool reach = count ? n + c[dg] >= S.R : acc + ms[dg] >= S.R;
+      if (c[dg] > 0 && reach) break;
       acc += ms[dg];
       n += c[dg];
     }
@@ -739,8 +540,8 @@ __global__ void token_step_kernel(int G, int pass, float tau, TokState* __restri
     if (pass == 3 && !S.select_all) {
       // all tied pairs share one score, hence one fixed-point mass
       const unsigned long long e1 = S.tie_mass / S.tie_cnt;
-      const unsigned long long need = S.R - S.above_mass;
-      unsigned long long t = e1 ? (need + e1 - 1) / e1 : 1;
+      const unsigned long long need = S.R - (count ? S.above_cnt : S.above_mass);
+      unsigned long long t = count ? need : (e1 ? (need + e1 - 1) / e1 : 1);
       if (t < 1) t = 1;
       if (t > S.tie_cnt) t = S.tie_cnt;
       S.take = uint32_t(t);
@@ -754,18 +555,18 @@ __global__ void token_step_kernel(int G, int pass, float tau, TokState* __restri
 }
 
 // Tied pairs (key equal to the cut) per chunk, when only some of them are taken.
-__global__ __launch_bounds__(256) void token_ties_count_kernel(Geom g,
-                                                               const float* __restrict__ scores,
-                                                               const TokState* __restrict__ st,
-                                                               uint32_t* __restrict__ chunkcnt) {
+__global__ __launch_bounds__(256) void pool_ties_count_kernel(int rows, int Nb, int rpc,
+                                                              const float* __restrict__ scores,
+                                                              const PoolState* __restrict__ st,
+                                                              uint32_t* __restrict__ chunkcnt) {
   __shared__ uint32_t red[4];
   const int grp = blockIdx.y;
-  const TokState S = st[grp];
+  const PoolState S = st[grp];
   if (S.select_all || !S.need_rank) return;
   const int tid = threadIdx.x;
-  const size_t N = size_t(g.L) * g.Nb;
-  const size_t begin = size_t(blockIdx.x) * kTokChunk * g.Nb;
-  const size_t end = min(N, begin + size_t(kTokChunk) * g.Nb);
+  const size_t N = size_t(rows) * Nb;
+  const size_t begin = size_t(blockIdx.x) * rpc * Nb;
+  const size_t end = min(N, begin + size_t(rpc) * Nb);
   const float* s = scores + size_t(grp) * N;
   uint32_t n = 0;
   for (size_t idx = begin + tid; idx < end; idx += 256) n += order_key(s[idx]) == S.prefix;
@@ -776,9 +577,9 @@ __global__ __launch_bounds__(256) void token_ties_count_kernel(Geom g,
 }
 
 // Exclusive scan of the per-chunk tie counts of one head group (one workgroup each).
-__global__ __launch_bounds__(256) void token_ties_scan_kernel(int nchunks,
-                                                              const TokState* __restrict__ st,
-                                                              uint32_t* __restrict__ chunkcnt) {
+__global__ __launch_bounds__(256) void pool_ties_scan_kernel(int nchunks,
+                                                             const PoolState* __restrict__ st,
+                                                             uint32_t* __restrict__ chunkcnt) {
   __shared__ uint32_t part[256];
   const int grp = blockIdx.x;
   if (st[grp].select_all || !st[grp].need_rank) return;
@@ -799,30 +600,32 @@ __global__ __launch_bounds__(256) void token_ties_scan_kernel(int nchunks,
   }
 }
 
-// Token mask, union bitmap and pair count.  Wave w of a chunk handles its tokens
-// kTokChunk/4 * w .. in order; each token's N_b pairs go 64 per ballot.
-__global__ __launch_bounds__(256) void token_emit_kernel(Geom g, const float* __restrict__ scores,
-                                                         TokState* __restrict__ st,
-                                                         const uint32_t* __restrict__ chunkoff,
-                                                         uint32_t* __restrict__ tokmask,
-                                                         uint32_t* __restrict__ qbits) {
-  constexpr int TPW = kTokChunk / 4;
+// Row bitmap, union bitmap (token rows) and pair count.  Wave w of a chunk handles its
+// quarter of the chunk's rows in order; each row's N_b pairs go 64 per ballot.
+template <bool TOKROWS>
+__global__ __launch_bounds__(256) void pool_emit_kernel(Geom g, int rows, int rpc,
+                                                        const float* __restrict__ scores,
+                                                        PoolState* __restrict__ st,
+                                                        const uint32_t* __restrict__ chunkoff,
+                                                        uint32_t* __restrict__ rowbits,
+                                                        uint32_t* __restrict__ qbits) {
   __shared__ uint32_t wties[4];
   const int grp = blockIdx.y;
-  const TokState S = st[grp];
+  const PoolState S = st[grp];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const bool all = S.select_all != 0;
   const uint32_t kstar = S.prefix;
   const uint32_t take = all ? 0u : S.take;
   const bool ranked = !all && S.need_rank;
   const int Nb = g.Nb, W = (Nb + 31) / 32;
-  const size_t N = size_t(g.L) * Nb;
+  const size_t N = size_t(rows) * Nb;
   const float* s = scores + size_t(grp) * N;
-  const int x0 = blockIdx.x * kTokChunk + w * TPW;
-  const int x1 = min(g.L, x0 + TPW);
+  const int rpw = rpc / 4;
+  const int x0 = blockIdx.x * rpc + w * rpw;
+  const int x1 = min(rows, x0 + rpw);
   const unsigned long long lt = (1ull << lane) - 1ull;
   uint32_t rank = 0;
-  if (ranked) {   // ties before this wave's tokens: earlier chunks, then earlier waves
+  if (ranked) {   // ties before this wave's rows: earlier chunks, then earlier waves
     uint32_t n = 0;
     for (int x = x0; x < x1; ++x)
       for (int jc = 0; jc < Nb; jc += 64) {
@@ -836,8 +639,8 @@ __global__ __launch_bounds__(256) void token_emit_kernel(Geom g, const float* __
   }
   uint32_t nnz = 0;
   for (int x = x0; x < x1; ++x) {
-    const int bx = token_block(g, x);
-    uint32_t* tm = tokmask + (size_t(grp) * g.L + x) * W;
+    const int bx = TOKROWS ? token_block(g, x) : x;   // the row's forced column
+    uint32_t* rb = rowbits + (size_t(grp) * rows + x) * W;
     uint32_t* qb = qbits + (size_t(grp) * Nb + bx) * W;
     for (int jc = 0; jc < Nb; jc += 64) {
       const int j = jc + lane;
@@ -854,19 +657,21 @@ __global__ __launch_bounds__(256) void token_emit_kernel(Geom g, const float* __
       const int wd = (jc >> 5) + (lane & 1);
       const uint32_t word = (lane & 1) ? uint32_t(sb >> 32) : uint32_t(sb);
       if (lane < 2 && wd < W) {
-        tm[wd] = word;
-        if (word) atomicOr(&qb[wd], word);
+        rb[wd] = word;
+        if (TOKROWS && word) atomicOr(&qb[wd], word);
       }
     }
   }
   if (lane == 0 && nnz) atomicAdd(&st[grp].nnz, nnz);
 }
 
-__global__ void token_stats_kernel(int G, double npairs, const TokState* __restrict__ st,
-                                   float* __restrict__ head_stats) {
+// head_stats = {k*, nnz, prefix mass, cutoff score}; and, if asked, the normalised scores.
+__global__ void pool_stats_kernel(int G, double npairs, double unit,
+                                  const PoolState* __restrict__ st,
+                                  float* __restrict__ head_stats) {
   const int grp = blockIdx.x * blockDim.x + threadIdx.x;
   if (grp >= G) return;
-  const TokState& S = st[grp];
+  const PoolState& S = st[grp];
   float* hs = head_stats + size_t(grp) * 4;
   if (S.select_all) {
     hs[0] = float(npairs);
@@ -880,6 +685,74 @@ __global__ void token_stats_kernel(int G, double npairs, const TokState* __restr
     hs[3] = float(double(e1) / z);
   }
   hs[1] = float(S.nnz);
+}
+
+__global__ void pool_norm_kernel(int N, double unit, const float* __restrict__ scores,
+                                 const PoolState* __restrict__ st, float* __restrict__ out) {
+  const int grp = blockIdx.y;
+  const float m = key_to_float(st[grp].mkey);
+  const float inv_z = float(unit / double(st[grp].Z));
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256)
+    out[size_t(grp) * N + i] = expf(scores[size_t(grp) * N + i] - m) * inv_z;
+}
+
+// Workspace of a pool selection, in this order (256-byte aligned): scores fp32
+// [G][rows][N_b], PoolState [G], histogram counts u32 [G][256], masses u64 [G][256],
+// per-chunk tie counts u32 [G][chunks], union bitmap u32 [G][N_b][W] (token rows only).
+struct PoolWs {
+  float* scores;
+  PoolState* state;
+  uint32_t* hcnt;
+  unsigned long long* hmass;
+  uint32_t* chunkcnt;
+  uint32_t* qbits;
+  size_t bytes;
+};
+
+static PoolWs pool_ws(void* ws, int G, int rows, int Nb, int rpc, bool tokrows) {
+  const size_t W = (size_t(Nb) + 31) / 32;
+  const size_t chunks = (size_t(rows) + rpc - 1) / rpc;
+  PoolWs w{};
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.scores = reinterpret_cast<float*>(take(size_t(G) * rows * Nb * 4));
+  w.state = reinterpret_cast<PoolState*>(take(size_t(G) * sizeof(PoolState)));
+  w.hcnt = reinterpret_cast<uint32_t*>(take(size_t(G) * 256 * 4));
+  w.hmass = reinterpret_cast<unsigned long long*>(take(size_t(G) * 256 * 8));
+  w.chunkcnt = reinterpret_cast<uint32_t*>(take(size_t(G) * chunks * 4));
+  w.qbits = reinterpret_cast<uint32_t*>(take(tokrows ? size_t(G) * Nb * W * 4 : 0));
+  w.bytes = off;
+  return w;
+}
+
+// Histogram passes, tie ranks and the row bitmap of a pool whose scores and maximum are
+// in place (state zeroed before the scores).
+template <bool TOKROWS>
+static int run_pool(const Geom& g, const PoolWs& w, int rows, int rpc, float tau, int topk,
+                    uint32_t* rowbits, hipStream_t st) {
+  const int G = g.B * g.Hh;
+  const int chunks = (rows + rpc - 1) / rpc;
+  const double npairs = double(rows) * g.Nb;
+  const double unit = pool_unit(npairs);
+  const dim3 cgrid(chunks, G);
+  const int sblocks = (G + 63) / 64;
+  for (int pass = 0; pass < 4; ++pass) {
+    pool_hist_kernel<<<cgrid, 256, 0, st>>>(rows, g.Nb, rpc, 24 - 8 * pass, unit, w.scores,
+                                            w.state, w.hcnt, w.hmass);
+    pool_step_kernel<<<sblocks, 64, 0, st>>>(G, pass, tau, topk, npairs, w.state, w.hcnt,
+                                             w.hmass);
+  }
+  pool_ties_count_kernel<<<cgrid, 256, 0, st>>>(rows, g.Nb, rpc, w.scores, w.state,
+                                                w.chunkcnt);
+  pool_ties_scan_kernel<<<G, 256, 0, st>>>(chunks, w.state, w.chunkcnt);
+  pool_emit_kernel<TOKROWS><<<cgrid, 256, 0, st>>>(g, rows, rpc, w.scores, w.state,
+                                                   w.chunkcnt, rowbits, w.qbits);
+  return launch_status();
 }
 
 template <bool TOPK>
@@ -901,6 +774,24 @@ static int launch_local(const Geom& g, float tau, int topk, const float* scores,
   return launch_status();
 }
 
+// Rows per chunk of the block pool's passes (one query-block row per wave).
+constexpr int kBlockRpc = 4;
+// Rows per chunk of the token pool's passes.
+constexpr int kTokenRpc = 64;
+
+// Workspace of vmoba_select / vmoba_select_mode: the global strategies use the pool
+// tables and a row bitmap behind them; the local ones the scores, a row bitmap and three
+// floats per row.  Scores come first in both.
+size_t select_ws(const Geom& g) {
+  const int G = g.B * g.Hh;
+  const size_t W = (size_t(g.Nb) + 31) / 32;
+  const size_t bitmap = align256(size_t(G) * g.Nb * W * 4);
+  const size_t global = pool_ws(nullptr, G, g.Nb, g.Nb, kBlockRpc, false).bytes + bitmap;
+  const size_t local = align256(size_t(G) * g.Nb * g.Nb * 4) + bitmap +
+                       align256(size_t(G) * g.Nb * 3 * 4);
+  return std::max(global, local);
+}
+
 int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int mode, float tau,
                   int topk, int32_t* row_ptr, int32_t* col_idx, int32_t* col_ptr,
                   int32_t* row_idx, float* head_stats, float* norm_scores, void* ws,
@@ -918,24 +809,32 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
   int stt = launch_status();
   if (stt) return stt;
   const int max_lds = int(size_t(kMaxBlocks) * kMaxBlocks / 8);
+  const size_t W = (size_t(g.Nb) + 31) / 32;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
+    return VMOBA_ERR_HIP;
   if (mode == VMOBA_SEL_THRESHOLD_GLOBAL || mode == VMOBA_SEL_TOPK_GLOBAL) {
-    const size_t words = ((nb2 + 1023) / 1024) * 32;  // whole 1024-pair chunks
-    const bool tk = mode == VMOBA_SEL_TOPK_GLOBAL;
-    const void* fn = tk ? reinterpret_cast<const void*>(global_select_kernel<true>)
-                        : reinterpret_cast<const void*>(global_select_kernel<false>);
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) !=
-        hipSuccess)
-      return VMOBA_ERR_HIP;
-    if (tk)
-      global_select_kernel<true><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
-          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
-    else
-      global_select_kernel<false><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
-          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+    const PoolWs w = pool_ws(ws, groups, g.Nb, g.Nb, kBlockRpc, false);
+    uint32_t* bitmap = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + w.bytes);
+    const size_t zero_words = (reinterpret_cast<unsigned char*>(w.chunkcnt) -
+                               reinterpret_cast<unsigned char*>(w.state)) / 4;
+    fill_zero_kernel<<<64, 256, 0, st>>>(reinterpret_cast<uint32_t*>(w.state), zero_words);
+    const int N = int(nb2);
+    pool_max_kernel<<<dim3(std::min(64, (N + 255) / 256), groups), 256, 0, st>>>(N, scores,
+                                                                              w.state);
+    const int k = mode == VMOBA_SEL_TOPK_GLOBAL ? topk : 0;
+    if ((stt = run_pool<false>(g, w, g.Nb, kBlockRpc, tau, k, bitmap, st))) return stt;
+    emit_lists_kernel<<<groups, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
+        g.Nb, bitmap, nullptr, row_ptr, col_idx, col_ptr, row_idx, nullptr);
+    const double npairs = double(nb2);
+    pool_stats_kernel<<<(groups + 63) / 64, 64, 0, st>>>(groups, npairs, pool_unit(npairs),
+                                                        w.state, head_stats);
+    if (norm_scores)
+      pool_norm_kernel<<<dim3(std::min(64, (N + 255) / 256), groups), 256, 0, st>>>(
+          N, pool_unit(npairs), scores, w.state, norm_scores);
     return launch_status();
   }
   // local strategies: bitmap and row statistics behind the scores in the workspace
-  const size_t W = (size_t(g.Nb) + 31) / 32;
   unsigned char* base = static_cast<unsigned char*>(ws);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + align256(groups * nb2 * sizeof(float)));
   float* rowstats = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(bitmap) +
@@ -944,23 +843,13 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
             ? launch_local<true>(g, tau, topk, scores, bitmap, rowstats, norm_scores, st)
             : launch_local<false>(g, tau, topk, scores, bitmap, rowstats, norm_scores, st);
   if (stt) return stt;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
-    return VMOBA_ERR_HIP;
   emit_lists_kernel<<<groups, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
       g.Nb, bitmap, rowstats, row_ptr, col_idx, col_ptr, row_idx, head_stats);
   return launch_status();
 }
 
-// Workspace of the token-granular selection, in this order (256-byte aligned):
-// scores fp32 [G][L][N_b], TokState [G], histogram counts u32 [G][256], masses u64
-// [G][256], per-chunk tie counts u32 [G][chunks], union bitmap u32 [G][N_b][W].
 size_t token_select_ws(const Geom& g) {
-  const size_t G = size_t(g.B) * g.Hh;
-  const size_t W = (size_t(g.Nb) + 31) / 32;
-  const size_t chunks = (size_t(g.L) + kTokChunk - 1) / kTokChunk;
-  return align256(G * g.L * g.Nb * 4) + align256(G * sizeof(TokState)) + align256(G * 256 * 4) +
-         align256(G * 256 * 8) + align256(G * chunks * 4) + align256(G * g.Nb * W * 4);
+  return pool_ws(nullptr, g.B * g.Hh, g.L, g.Nb, kTokenRpc, true).bytes;
 }
 
 int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, float tau,
@@ -970,51 +859,32 @@ int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, floa
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int G = g.B * g.Hh;
   const size_t W = (size_t(g.Nb) + 31) / 32;
-  const int chunks = (g.L + kTokChunk - 1) / kTokChunk;
-  unsigned char* p = static_cast<unsigned char*>(ws);
-  float* scores = reinterpret_cast<float*>(p);
-  p += align256(size_t(G) * g.L * g.Nb * 4);
-  TokState* state = reinterpret_cast<TokState*>(p);
-  p += align256(size_t(G) * sizeof(TokState));
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(G) * 256 * 4);
-  unsigned long long* hmass = reinterpret_cast<unsigned long long*>(p);
-  p += align256(size_t(G) * 256 * 8);
-  uint32_t* chunkcnt = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(G) * chunks * 4);
-  uint32_t* qbits = reinterpret_cast<uint32_t*>(p);
-  // zero the state, the histograms and the union bitmap (a fill kernel, not a memset)
-  const size_t zero_words =
-      (reinterpret_cast<unsigned char*>(chunkcnt) - reinterpret_cast<unsigned char*>(state)) / 4;
-  fill_zero_kernel<<<1024, 256, 0, st>>>(reinterpret_cast<uint32_t*>(state), zero_words);
-  fill_zero_kernel<<<1024, 256, 0, st>>>(qbits, size_t(G) * g.Nb * W);
+  const PoolWs w = pool_ws(ws, G, g.L, g.Nb, kTokenRpc, true);
+  // zero the state, the histograms and the union bitmap (fill kernels, not memsets)
+  const size_t zero_words = (reinterpret_cast<unsigned char*>(w.chunkcnt) -
+                             reinterpret_cast<unsigned char*>(w.state)) / 4;
+  fill_zero_kernel<<<64, 256, 0, st>>>(reinterpret_cast<uint32_t*>(w.state), zero_words);
+  fill_zero_kernel<<<1024, 256, 0, st>>>(w.qbits, size_t(G) * g.Nb * W);
   const float scale = 1.0f / sqrtf(float(g.D));
   const dim3 sgrid((g.L + 31) / 32, (g.Nb + 31) / 32, G);
   if (g.D == 128)
     token_scores_kernel<128, uint16_t><<<sgrid, 64, 0, st>>>(
-        g, static_cast<const uint16_t*>(q), k_pool, scores, state, scale);
+        g, static_cast<const uint16_t*>(q), k_pool, w.scores, w.state, scale);
   else
     token_scores_kernel<64, uint16_t><<<sgrid, 64, 0, st>>>(
-        g, static_cast<const uint16_t*>(q), k_pool, scores, state, scale);
+        g, static_cast<const uint16_t*>(q), k_pool, w.scores, w.state, scale);
   int stt = launch_status();
   if (stt) return stt;
-  const dim3 cgrid(chunks, G);
-  const int sblocks = (G + 63) / 64;
-  for (int pass = 0; pass < 4; ++pass) {
-    token_hist_kernel<<<cgrid, 256, 0, st>>>(g, 24 - 8 * pass, scores, state, hcnt, hmass);
-    token_step_kernel<<<sblocks, 64, 0, st>>>(G, pass, tau, state, hcnt, hmass);
-  }
-  token_ties_count_kernel<<<cgrid, 256, 0, st>>>(g, scores, state, chunkcnt);
-  token_ties_scan_kernel<<<G, 256, 0, st>>>(chunks, state, chunkcnt);
-  token_emit_kernel<<<cgrid, 256, 0, st>>>(g, scores, state, chunkcnt, tokmask, qbits);
-  if ((stt = launch_status())) return stt;
+  if ((stt = run_pool<true>(g, w, g.L, kTokenRpc, tau, 0, tokmask, st))) return stt;
   const int max_lds = int(size_t(kMaxBlocks) * kMaxBlocks / 8);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
     return VMOBA_ERR_HIP;
   emit_lists_kernel<<<G, kSelThreads, size_t(g.Nb) * W * 4, st>>>(
-      g.Nb, qbits, nullptr, row_ptr, col_idx, col_ptr, row_idx, nullptr);
-  token_stats_kernel<<<sblocks, 64, 0, st>>>(G, double(g.L) * g.Nb, state, head_stats);
+      g.Nb, w.qbits, nullptr, row_ptr, col_idx, col_ptr, row_idx, nullptr);
+  const double npairs = double(g.L) * g.Nb;
+  pool_stats_kernel<<<(G + 63) / 64, 64, 0, st>>>(G, npairs, pool_unit(npairs), w.state,
+                                                  head_stats);
   return launch_status();
 }
 

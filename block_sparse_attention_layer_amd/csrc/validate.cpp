@@ -66,22 +66,17 @@ Geom make_geom(const vmoba_problem* p) {
 int workspace_bytes(const vmoba_problem* p, int op, size_t* bytes) {
   const Geom g = make_geom(p);
   const size_t groups = size_t(g.B) * g.Hh;
-  const size_t pool = size_t(g.Nb) * g.Nb;
   switch (op) {
     case VMOBA_OP_POOL:
     case VMOBA_OP_SPARSE_FWD:
     case VMOBA_OP_DENSE_FWD:
       *bytes = 0;
       return VMOBA_OK;
-    case VMOBA_OP_SELECT: {
-      // raw block scores, fp32 per head group; the local modes add a row-aligned pair
-      // bitmap and three floats of statistics per row
-      const size_t words = (size_t(g.Nb) + 31) / 32;
-      *bytes = align256(groups * pool * sizeof(float)) +
-               align256(groups * size_t(g.Nb) * words * 4) +
-               align256(groups * size_t(g.Nb) * 3 * sizeof(float));
+    case VMOBA_OP_SELECT:
+      // block scores, fp32 per head group, then the pool tables and a row bitmap (global
+      // strategies) or a row bitmap and three floats per row (local ones)
+      *bytes = select_ws(g);
       return VMOBA_OK;
-    }
     case VMOBA_OP_SPARSE_BWD:
     case VMOBA_OP_DENSE_BWD:
       // delta = rowsum(dO * O), fp32 [B][Hh][L]
