@@ -492,15 +492,27 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(int rows, int Nb, int rp
 }
 
 // After digit pass `pass`: pick the digit where the running mass (topk > 0: count)
-// reaches the target, and clear the histogram for the next pass.  One thread per group.
-__global__ void pool_step_kernel(int G, int pass, float tau, int topk, double npairs,
-                                 PoolState* __restrict__ st, uint32_t* __restrict__ hcnt,
-                                 unsigned long long* __restrict__ hmass) {
-  const int grp = blockIdx.x * blockDim.x + threadIdx.x;
-  if (grp >= G) return;
+// reaches the target.  One wave per head group: the lanes copy the merged histogram to
+// LDS and clear it for the next pass, then lane 0 walks the copy.
+__global__ __launch_bounds__(64) void pool_step_kernel(int pass, float tau, int topk,
+                                                       double npairs,
+                                                       PoolState* __restrict__ st,
+                                                       uint32_t* __restrict__ hcnt,
+                                                       unsigned long long* __restrict__ hmass) {
+  __shared__ uint32_t c[256];
+  __shared__ unsigned long long ms[256];
+  const int grp = blockIdx.x, lane = threadIdx.x;
+  uint32_t* gc = hcnt + grp * 256;
+  unsigned long long* gm = hmass + grp * 256;
+  for (int d = lane; d < 256; d += 64) {
+    c[d] = gc[d];
+    ms[d] = gm[d];
+    gc[d] = 0u;
+    gm[d] = 0ull;
+  }
+  __syncthreads();
+  if (lane != 0) return;
   PoolState& S = st[grp];
-  uint32_t* c = hcnt + grp * 256;
-  unsigned long long* ms = hmass + grp * 256;
   const bool count = topk > 0;
   if (pass == 0) {   // every pair matched: the histogram holds the whole pool
     unsigned long long z = 0;
@@ -517,40 +529,35 @@ __global__ void pool_step_kernel(int G, int pass, float tau, int topk, double np
     S.above_cnt = 0;
     S.prefix = 0;
   }
-  if (!S.select_all) {
-    const int shift = 24 - 8 * pass;
-    unsigned long long acc = S.above_mass;
-    uint32_t n = S.above_cnt;
-    int dg = 255;
-    for (; dg >= 0; --dg) {
-      const bool reach = count ? n + c[dg] >= S.R : acc + ms[dg] >= S.R;
-      if (c[dg] > 0 && reach) break;
-      acc += ms[dg];
-      n += c[dg];
-    }
-    if (dg < 0) {
-      S.select_all = 1u;   // rounding kept the total below the target
-    } else {
-      S.above_mass = acc;
-      S.above_cnt = n;
-      S.prefix |= uint32_t(dg) << shift;
-      S.tie_cnt = c[dg];
-      S.tie_mass = ms[dg];
-    }
-    if (pass == 3 && !S.select_all) {
-      // all tied pairs share one score, hence one fixed-point mass
-      const unsigned long long e1 = S.tie_mass / S.tie_cnt;
-      const unsigned long long need = S.R - (count ? S.above_cnt : S.above_mass);
-      unsigned long long t = count ? need : (e1 ? (need + e1 - 1) / e1 : 1);
-      if (t < 1) t = 1;
-      if (t > S.tie_cnt) t = S.tie_cnt;
-      S.take = uint32_t(t);
-      S.need_rank = S.take < S.tie_cnt ? 1u : 0u;
-    }
+  if (S.select_all) return;
+  const int shift = 24 - 8 * pass;
+  unsigned long long acc = S.above_mass;
+  uint32_t n = S.above_cnt;
+  int dg = 255;
+  for (; dg >= 0; --dg) {
+    const bool reach = count ? n + c[dg] >= S.R : acc + ms[dg] >= S.R;
+    if (c[dg] > 0 && reach) break;
+    acc += ms[dg];
+    n += c[dg];
   }
-  for (int d = 0; d < 256; ++d) {
-    c[d] = 0;
-    ms[d] = 0;
+  if (dg < 0) {
+    S.select_all = 1u;   // rounding kept the total below the target
+    return;
+  }
+  S.above_mass = acc;
+  S.above_cnt = n;
+  S.prefix |= uint32_t(dg) << shift;
+  S.tie_cnt = c[dg];
+  S.tie_mass = ms[dg];
+  if (pass == 3) {
+    // all tied pairs share one score, hence one fixed-point mass
+    const unsigned long long e1 = S.tie_mass / S.tie_cnt;
+    const unsigned long long need = S.R - (count ? S.above_cnt : S.above_mass);
+    unsigned long long t = count ? need : (e1 ? (need + e1 - 1) / e1 : 1);
+    if (t < 1) t = 1;
+    if (t > S.tie_cnt) t = S.tie_cnt;
+    S.take = uint32_t(t);
+    S.need_rank = S.take < S.tie_cnt ? 1u : 0u;
   }
 }
 
@@ -740,12 +747,10 @@ static int run_pool(const Geom& g, const PoolWs& w, int rows, int rpc, float tau
   const double npairs = double(rows) * g.Nb;
   const double unit = pool_unit(npairs);
   const dim3 cgrid(chunks, G);
-  const int sblocks = (G + 63) / 64;
   for (int pass = 0; pass < 4; ++pass) {
     pool_hist_kernel<<<cgrid, 256, 0, st>>>(rows, g.Nb, rpc, 24 - 8 * pass, unit, w.scores,
                                             w.state, w.hcnt, w.hmass);
-    pool_step_kernel<<<sblocks, 64, 0, st>>>(G, pass, tau, topk, npairs, w.state, w.hcnt,
-                                             w.hmass);
+    pool_step_kernel<<<G, 64, 0, st>>>(pass, tau, topk, npairs, w.state, w.hcnt, w.hmass);
   }
   pool_ties_count_kernel<<<cgrid, 256, 0, st>>>(rows, g.Nb, rpc, w.scores, w.state,
                                                 w.chunkcnt);
