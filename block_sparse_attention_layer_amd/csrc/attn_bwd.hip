@@ -509,10 +509,8 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     }
     const unsigned char* kb = cur;
     const unsigned char* vb = cur + TILE;
-    // While direct-to-LDS loads are in flight the compiler waits for every outstanding LDS
-    // read at the first use of any of them, so reads are issued in batches: the K and V
-    // fragments of half the d-steps, their products, the other half, and the K^T reads of
-    // dQ right after.
+    // K and V fragments in four batches of d-steps, each read ahead of its products, and
+    // the K^T reads of dQ right after.
     f32x16 sacc[KSUB], dpacc[KSUB];
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk)
@@ -521,7 +519,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
         sacc[kk][v] = 0.f;
         dpacc[kk][v] = 0.f;
       }
-    constexpr int NB = TOK ? 4 : 2;   // batches (more, smaller ones with the token mask)
+    constexpr int NB = 4;   // batches of d-steps
 #pragma unroll
     for (int hb = 0; hb < NB; ++hb) {
       constexpr int HS = D / 16 / NB;   // d-steps per batch

@@ -531,14 +531,13 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int m = 0; m < M; ++m) sacc[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 ka[2][D / 32];   // all K fragments of the tile first: one LDS wait, not eight
+    bf16x8 ka[2][D / 32];   // the tile's K fragments, read ahead of their products
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int s = 0; s < D / 32; ++s)
         ka[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
             sm + ks * 16 * ROWB + krd + 16 * ((4 * s + g16) ^ i16)));
-    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their products
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -547,9 +546,7 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
         for (int m = 0; m < M; ++m)
           sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks][s], qf[m][s], sacc[ks][m],
                                                                 0, 0, 0);
-    // V^T fragments, issued once the K fragments are dead: the compiler waits for every
-    // LDS read before the first use of a transposing read's result, so they must be in
-    // flight long before the products that need them
+    // V^T fragments, read here so that their latency hides behind the softmax
     bf16x8 va[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
@@ -558,7 +555,6 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
       const u32x2 hi = lds_read_tr16(sm + o + 16 * ROWB);
       va[ds] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    __builtin_amdgcn_sched_barrier(0);
     if (t * KT + KT > nkeys) {   // ragged last tile: keys past the end score -inf
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)

@@ -19,7 +19,9 @@
 //   3. The prefix plus the diagonal go to a row bitmap (wave ballots in linear order),
 //      and emit_lists_kernel turns the bitmap into CSR and CSC (row and column counts, an
 //      exclusive scan, an ascending walk per row / column).
-// The same passes select over the token-granular pool (query tokens x key blocks).
+// Up to kSingleSelectBlocks blocks, single_select_kernel does all of this in one
+// workgroup per head group, in LDS.  The pool passes also select over the token-granular
+// pool (query tokens x key blocks).
 //
 // Local strategies (threshold + local, top-k + local): every query block's row of N_b
 // scores is its own pool, normalised by a softmax over the row.  select_local_kernel
@@ -91,10 +93,17 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float m) {
   return uint64_t(double(e) * kMassUnit + 0.5);
 }
 
-// Shared memory of emit_lists_kernel.
+// Shared memory of single_select_kernel and emit_lists_kernel.
 struct SelShared {
+  uint32_t cnt[256];
+  unsigned long long mass[256];
   float redf[kSelWaves];
+  unsigned long long redu[kSelWaves];
   uint32_t redi[kSelWaves];
+  // selection state (written by thread 0)
+  float m;
+  unsigned long long Z, R, above_mass, tie_mass;
+  uint32_t prefix, above_cnt, tie_cnt, take_ties, select_all, tie_seen;
   int32_t row_cnt[kMaxBlocks];
   int32_t col_cnt[kMaxBlocks];
 };
@@ -127,6 +136,33 @@ __device__ __forceinline__ void histogram_add(uint32_t* cnt, unsigned long long*
   }
 }
 
+__device__ __forceinline__ void histogram_add(SelShared& sh, bool match, uint32_t dg,
+                                              unsigned long long mass) {
+  histogram_add(sh.cnt, sh.mass, match, dg, mass);
+}
+
+__device__ float block_max(float v, SelShared& sh) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh.redf[w] = v;
+  __syncthreads();
+  float r = sh.redf[0];
+  for (int i = 1; i < kSelWaves; ++i) r = fmaxf(r, sh.redf[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ unsigned long long block_sum_u64(unsigned long long v, SelShared& sh) {
+  v = wave_sum_u64(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh.redu[w] = v;
+  __syncthreads();
+  unsigned long long r = 0;
+  for (int i = 0; i < kSelWaves; ++i) r += sh.redu[i];
+  __syncthreads();
+  return r;
+}
+
 // Exclusive scan of one int per thread (thread order); returns the block total in *total.
 __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -146,6 +182,205 @@ __device__ int block_excl_scan(int v, SelShared& sh, int* total) {
   __syncthreads();
   *total = tot;
   return off + x - v;
+}
+
+// The global strategies for small pools (N_b <= kSingleSelectBlocks): one 1024-thread
+// workgroup per head group runs the whole decision in LDS: max and total mass, the four
+// digit passes, ties in linear order into an LDS pair bitmap, then CSR and CSC.  Below a
+// few hundred blocks this beats the pool passes, whose dozen dependent launches cost more
+// than the pool itself.
+template <bool TOPK>
+__global__ __launch_bounds__(kSelThreads) void single_select_kernel(
+    int Nb, float tau, int topk, const float* __restrict__ scores, int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx, int32_t* __restrict__ col_ptr,
+    int32_t* __restrict__ row_idx, float* __restrict__ head_stats,
+    float* __restrict__ norm_scores) {
+  __shared__ SelShared sh;
+  extern __shared__ uint32_t bits[];  // N_b*N_b-bit pair bitmap, padded to 64-bit words
+  const int grp = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int N = Nb * Nb;
+  const float* s = scores + size_t(grp) * N;
+
+  // 1. max and total fixed-point mass
+  float mx = -INFINITY;
+  for (int idx = tid; idx < N; idx += kSelThreads) mx = fmaxf(mx, s[idx]);
+  mx = block_max(mx, sh);
+  unsigned long long z = 0;
+  for (int idx = tid; idx < N; idx += kSelThreads) z += fixed_mass(s[idx], mx);
+  z = block_sum_u64(z, sh);
+  if (tid == 0) {
+    sh.m = mx;
+    sh.Z = z;
+    if constexpr (TOPK) {
+      sh.R = (unsigned long long)topk;   // a count of pairs
+      sh.select_all = topk >= N ? 1u : 0u;
+    } else {
+      const double r = ceil(double(tau) * double(z));
+      sh.R = (unsigned long long)r;
+      sh.select_all = (tau >= 1.0f || sh.R > z) ? 1u : 0u;
+    }
+    sh.prefix = 0;
+    sh.above_cnt = 0;
+    sh.above_mass = 0;
+  }
+  __syncthreads();
+
+  // 2. four radix passes over the order keys, most significant digit first
+  if (!sh.select_all) {
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t hi_mask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
+      for (int d = tid; d < 256; d += kSelThreads) {
+        sh.cnt[d] = 0;
+        sh.mass[d] = 0;
+      }
+      __syncthreads();
+      const uint32_t prefix = sh.prefix;
+      for (int base = 0; base < N; base += kSelThreads) {
+        const int idx = base + tid;
+        const float sv = idx < N ? s[idx] : -INFINITY;
+        const uint32_t key = order_key(sv);
+        const bool match = idx < N && (key & hi_mask) == prefix;
+        const uint32_t dg = (key >> shift) & 0xffu;
+        const unsigned long long ms = match ? fixed_mass(sv, mx) : 0ull;
+        histogram_add(sh, match, dg, ms);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned long long acc = sh.above_mass;
+        uint32_t cnt = sh.above_cnt;
+        int dg = 255;
+        for (; dg >= 0; --dg) {
+          const bool reach = TOPK ? cnt + sh.cnt[dg] >= sh.R : acc + sh.mass[dg] >= sh.R;
+          if (reach && sh.cnt[dg] > 0) break;
+          acc += sh.mass[dg];
+          cnt += sh.cnt[dg];
+        }
+        if (dg < 0) {
+          sh.select_all = 1u;  // rounding kept the total below the target
+        } else {
+          sh.above_mass = acc;
+          sh.above_cnt = cnt;
+          sh.prefix = prefix | (uint32_t(dg) << shift);
+          sh.tie_cnt = sh.cnt[dg];
+          sh.tie_mass = sh.mass[dg];
+        }
+      }
+      __syncthreads();
+      if (sh.select_all) break;
+    }
+  }
+  if (tid == 0 && !sh.select_all) {
+    // all tied pairs share one score, hence one fixed-point mass
+    const unsigned long long e1 = sh.tie_mass / sh.tie_cnt;
+    const unsigned long long need = sh.R - (TOPK ? sh.above_cnt : sh.above_mass);
+    unsigned long long t = TOPK ? need : (e1 ? (need + e1 - 1) / e1 : 1);
+    if (t < 1) t = 1;
+    if (t > sh.tie_cnt) t = sh.tie_cnt;
+    sh.take_ties = uint32_t(t);
+  }
+  if (tid == 0) sh.tie_seen = 0;
+  __syncthreads();
+
+  // 3. compaction in linear order into the LDS bitmap
+  const bool all = sh.select_all != 0;
+  const uint32_t kstar = sh.prefix;
+  const uint32_t take = all ? 0u : sh.take_ties;
+  const int lane = tid & 63, w = tid >> 6;
+  const float inv_z = float(kMassUnit / double(sh.Z));
+  for (int base = 0; base < N; base += kSelThreads) {
+    const int idx = base + tid;
+    const bool in = idx < N;
+    const float sv = in ? s[idx] : -INFINITY;
+    const uint32_t key = order_key(sv);
+    const bool tie = in && !all && key == kstar;
+    // rank of this tie among ties in linear order
+    const unsigned long long tmask = __ballot(tie);
+    const int before_in_wave = __popcll(tmask & ((1ull << lane) - 1ull));
+    if (lane == 0) sh.redi[w] = uint32_t(__popcll(tmask));
+    __syncthreads();
+    int before = int(sh.tie_seen);
+    int total = 0;
+    for (int i = 0; i < kSelWaves; ++i) {
+      if (i < w) before += int(sh.redi[i]);
+      total += int(sh.redi[i]);
+    }
+    const int rank = before + before_in_wave;
+    const int i_row = in ? idx / Nb : 0;
+    const bool diag = in && (idx - i_row * Nb) == i_row;
+    const bool sel = in && (all || key > kstar || (tie && uint32_t(rank) < take) || diag);
+    const unsigned long long smask = __ballot(sel);
+    if (lane == 0) {
+      const int word = (base >> 5) + 2 * w;
+      bits[word] = uint32_t(smask);
+      bits[word + 1] = uint32_t(smask >> 32);
+    }
+    if (norm_scores && in) norm_scores[size_t(grp) * N + idx] = expf(sv - sh.m) * inv_z;
+    __syncthreads();
+    if (tid == 0) sh.tie_seen += uint32_t(total);
+    __syncthreads();
+  }
+
+  // 4. CSR / CSC from the bitmap
+  for (int i = tid; i < Nb; i += kSelThreads) {
+    int rc = 0, cc = 0;
+    for (int j = 0; j < Nb; ++j) {
+      const int ir = i * Nb + j, ic = j * Nb + i;
+      rc += (bits[ir >> 5] >> (ir & 31)) & 1u;
+      cc += (bits[ic >> 5] >> (ic & 31)) & 1u;
+    }
+    sh.row_cnt[i] = rc;
+    sh.col_cnt[i] = cc;
+  }
+  __syncthreads();
+  int32_t* rp = row_ptr + size_t(grp) * (Nb + 1);
+  int32_t* cp = col_ptr + size_t(grp) * (Nb + 1);
+  // Nb <= kMaxBlocks = kSelThreads: one entry per thread
+  {
+    const int rc = tid < Nb ? sh.row_cnt[tid] : 0;
+    const int cc = tid < Nb ? sh.col_cnt[tid] : 0;
+    int rtot = 0, ctot = 0;
+    const int roff = block_excl_scan(rc, sh, &rtot);
+    const int coff = block_excl_scan(cc, sh, &ctot);
+    __syncthreads();
+    if (tid < Nb) {
+      sh.row_cnt[tid] = roff;
+      sh.col_cnt[tid] = coff;
+      rp[tid] = roff;
+      cp[tid] = coff;
+    }
+    if (tid == 0) {
+      rp[Nb] = rtot;
+      cp[Nb] = ctot;
+      if (head_stats) {
+        float* hs = head_stats + size_t(grp) * 4;
+        const double zz = double(sh.Z);
+        if (all) {
+          hs[0] = float(N);
+          hs[2] = 1.0f;
+          hs[3] = 0.0f;
+        } else {
+          const unsigned long long e1 = sh.tie_mass / sh.tie_cnt;
+          hs[0] = float(sh.above_cnt + sh.take_ties);
+          hs[2] = float(double(sh.above_mass + e1 * sh.take_ties) / zz);
+          hs[3] = float(double(e1) / zz);
+        }
+        hs[1] = float(rtot);
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* ci = col_idx + size_t(grp) * N;
+  int32_t* ri = row_idx + size_t(grp) * N;
+  for (int i = tid; i < Nb; i += kSelThreads) {
+    int pr = sh.row_cnt[i], pc = sh.col_cnt[i];
+    for (int j = 0; j < Nb; ++j) {
+      const int ir = i * Nb + j, ic = j * Nb + i;
+      if ((bits[ir >> 5] >> (ir & 31)) & 1u) ci[pr++] = j;
+      if ((bits[ic >> 5] >> (ic & 31)) & 1u) ri[pc++] = j;
+    }
+  }
 }
 
 // One wave per query-block row; U = ceil(N_b / 64) pairs per lane.  rowstats[G][N_b][3] =
@@ -781,6 +1016,8 @@ static int launch_local(const Geom& g, float tau, int topk, const float* scores,
 
 // Rows per chunk of the block pool's passes (one query-block row per wave).
 constexpr int kBlockRpc = 4;
+// Block counts up to which the global strategies run in one workgroup per head group.
+constexpr int kSingleSelectBlocks = 128;
 // Rows per chunk of the token pool's passes.
 constexpr int kTokenRpc = 64;
 
@@ -818,7 +1055,24 @@ int launch_select(const Geom& g, const float* q_pool, const float* k_pool, int m
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(emit_lists_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) != hipSuccess)
     return VMOBA_ERR_HIP;
-  if (mode == VMOBA_SEL_THRESHOLD_GLOBAL || mode == VMOBA_SEL_TOPK_GLOBAL) {
+  const bool global = mode == VMOBA_SEL_THRESHOLD_GLOBAL || mode == VMOBA_SEL_TOPK_GLOBAL;
+  if (global && g.Nb <= kSingleSelectBlocks) {
+    const size_t words = ((nb2 + 1023) / 1024) * 32;  // whole 1024-pair chunks
+    const bool tk = mode == VMOBA_SEL_TOPK_GLOBAL;
+    const void* fn = tk ? reinterpret_cast<const void*>(single_select_kernel<true>)
+                        : reinterpret_cast<const void*>(single_select_kernel<false>);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds) !=
+        hipSuccess)
+      return VMOBA_ERR_HIP;
+    if (tk)
+      single_select_kernel<true><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
+          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+    else
+      single_select_kernel<false><<<groups, kSelThreads, words * sizeof(uint32_t), st>>>(
+          g.Nb, tau, topk, scores, row_ptr, col_idx, col_ptr, row_idx, head_stats, norm_scores);
+    return launch_status();
+  }
+  if (global) {
     const PoolWs w = pool_ws(ws, groups, g.Nb, g.Nb, kBlockRpc, false);
     uint32_t* bitmap = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(ws) + w.bytes);
     const size_t zero_words = (reinterpret_cast<unsigned char*>(w.chunkcnt) -

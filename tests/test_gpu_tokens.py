@@ -35,6 +35,8 @@ CASES = [
     ("small2d_168", "l2d_32k", dict(T=7, H=18, W=12), LayerSpec(1, (7, 6, 4)), 128, 2),
     ("small1d_120", "l1d_32k", dict(T=6, H=10, W=12), LayerSpec(0, (1, 10, 12)), 128, 2),
     ("many_blocks_3d", "l3d_55k", dict(T=8, H=12, W=32), LayerSpec(2, (2, 2, 2)), 64, 2),
+    # the block-count limit: 1024 blocks of 8 tokens, 32 mask words per token
+    ("max_blocks_3d", "l3d_55k", dict(T=8, H=32, W=32), LayerSpec(2, (2, 2, 2)), 64, 1),
 ]
 IDS = [c[0] for c in CASES]
 
