@@ -40,6 +40,8 @@ def parse():
                     choices=["threshold_global", "topk_global", "threshold_local", "topk_local"],
                     help="selection strategy (the method's is threshold_global)")
     ap.add_argument("--topk", type=int, default=None, help="k of the top-k strategies")
+    ap.add_argument("--dit", action="store_true",
+                    help="time one synthetic DiT block (projections, MLP) around the layer")
     ap.add_argument("--granularity", default="block", choices=["block", "token"],
                     help="token: the token-granular query pool (prints its own line)")
     ap.add_argument("--sweep", action="store_true",
@@ -297,6 +299,91 @@ def run_tokens(workload, layer, tau, steps, warmup):
     print(json.dumps(line), flush=True)
 
 
+def run_dit(workload, layer, tau, steps, warmup, mlp_hidden=8960):
+    """One pre-norm DiT block at Wan 2.1 1.3B's sizes (dim = heads * d = 1536, MLP 8960)
+    around the layer, forward + backward in bf16 on the workload's latent: the sparse step
+    and the dense (warm-up) step, with the attention calls timed apart from the rest.
+    Prints one JSON line."""
+    import torch
+    from synthetic import CONFIGS, make_dit_input, make_dit_params
+    import block_sparse_attention_layer_amd as vm
+
+    cfg = CONFIGS[workload]
+    spec = cfg["layers"][layer]
+    if tau is None:
+        tau = 0.25 if 0.25 in cfg["taus"] else cfg["taus"][0]
+    dev = torch.device("cuda:0")
+    heads, d = cfg["heads"], cfg["head_dim"]
+    dim = heads * d
+    latent = (cfg["T"], cfg["H"], cfg["W"])
+    blocks = [None, None, None]
+    blocks[spec.layer_idx % 3] = tuple(spec.block)
+    T, H, W = latent
+    defaults = [(1, H, W), (T, H, W), (T, H, W)]   # unused modes: any valid shape
+    cyc = vm.LayerCycle(latent, *[b or defaults[i] for i, b in enumerate(blocks)])
+    blk = vm.SyntheticDiTBlock(dim, heads, mlp_hidden, spec.layer_idx, cyc, tau=tau,
+                               dtype=torch.bfloat16, device=dev)
+    blk.load_params({n: t.to(torch.bfloat16) for n, t in
+                     make_dit_params(dim, mlp_hidden, 1, seed=7000)[0].items()})
+    x, g = (t.to(dev, torch.bfloat16) for t in make_dit_input(cfg["batch"], latent, dim))
+
+    # time the attention calls inside the block with events around the library entry points
+    attn_ms = []
+    import block_sparse_attention_layer_amd.layer as lay
+    orig = {}
+    for name in ("vmoba_sparse_attn_fwd", "vmoba_sparse_attn_bwd", "vmoba_dense_attn_fwd",
+                 "vmoba_dense_attn_bwd", "select_blocks"):
+        fn = getattr(lay, name)
+        orig[name] = fn
+
+        def wrapped(*a, _fn=fn, **kw):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            out = _fn(*a, **kw)
+            e1.record()
+            attn_ms.append((e0, e1))
+            return out
+        setattr(lay, name, wrapped)
+
+    def run(full):
+        xg = x.detach().requires_grad_()
+        y = blk(xg, full=full)
+        y.backward(g)
+
+    out = {}
+    try:
+        for full in (False, True):
+            for _ in range(warmup):
+                run(full)
+            torch.cuda.synchronize()
+            attn_ms.clear()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                run(full)
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / steps
+            a = sum(e0.elapsed_time(e1) for e0, e1 in attn_ms) / steps
+            out["dense" if full else "sparse"] = (ms, a)
+    finally:
+        for name, fn in orig.items():
+            setattr(lay, name, fn)
+    (ms_s, a_s), (ms_d, a_d) = out["sparse"], out["dense"]
+    line = {
+        "metric": "DiT block fwd+bwd ms (VMoBA layer vs full attention)",
+        "config": {"workload": f"{workload} layer {layer}: latent {T}x{H}x{W} = {T * H * W} "
+                               f"tokens, dim {dim} ({heads} x {d}), MLP {mlp_hidden}, blocks "
+                               f"{tuple(spec.block)}, tau {tau}, bf16, synthetic weights"},
+        "steps": steps, "warmup": warmup,
+        "sparse_block_ms": round(ms_s, 3), "sparse_attention_ms": round(a_s, 3),
+        "dense_block_ms": round(ms_d, 3), "dense_attention_ms": round(a_d, 3),
+        "rest_of_block_ms": round(ms_s - a_s, 3),
+        "attention_share_sparse": round(a_s / ms_s, 3),
+        "attention_share_dense": round(a_d / ms_d, 3),
+        "block_speedup": round(ms_d / ms_s, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def describe(workload, r):
     p, spec = r["p"], r["spec"]
     sel = ("" if r.get("mode", "threshold_global") == "threshold_global"
@@ -342,6 +429,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         sweep(args)
+        return
+    if args.dit:
+        run_dit(args.workload, args.layer, args.tau, args.steps, args.warmup)
         return
     if args.granularity == "token":
         run_tokens(args.workload, args.layer, args.tau, args.steps, args.warmup)
