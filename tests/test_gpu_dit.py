@@ -159,3 +159,26 @@ def test_stack_bf16_own_selection_runs_the_layer_cycle():
         gm = masks_from_csr(s.row_ptr, s.col_idx, nb)
         assert (masks_from_csc(s.col_ptr, s.row_idx, nb) == gm).all()
         assert gm[:, np.arange(nb), np.arange(nb)].all()
+
+
+def test_block_fp32_batch2_matches_oracle():
+    """Two batch entries: each is its own pool (head groups g = b*Hh + h)."""
+    print("[dit block fp32 batch 2, 3D layer]", flush=True)
+    layer = 2
+    P = make_dit_params(DIM, HID, 3)[layer]
+    x, g = make_dit_input(2, LAT, DIM, seed=7150)
+    blk = SyntheticDiTBlock(DIM, HEADS, HID, layer, CYCLE, tau=0.25, dtype=torch.float32,
+                            device=DEV).load_params(P)
+    Po = {n: t.double().requires_grad_() for n, t in P.items()}
+    xo = x.double().requires_grad_()
+    yo, info = odit.dit_block(xo, Po, LAT, HEADS, layer, CYCLE.block(layer), tau=0.25)
+    (yo * g.double()).sum().backward()
+    xg = x.to(DEV).requires_grad_()
+    y = blk(xg, selection=csr_to_device(info["mask"], DEV))
+    y.backward(g.to(DEV))
+    torch.cuda.synchronize()
+    tol = 2e-4
+    assert _rel(y, yo) <= tol
+    assert _rel(xg.grad, xo.grad) <= tol
+    for mod, w in ((blk.q, "wq"), (blk.k, "wk"), (blk.v, "wv"), (blk.o, "wo")):
+        assert _rel(mod.weight.grad, Po[w].grad) <= tol, w

@@ -35,6 +35,8 @@ CASES = [
     ("small2d_168", "l2d_32k", dict(T=7, H=18, W=12), LayerSpec(1, (7, 6, 4)), 128, 2),
     ("small1d_120", "l1d_32k", dict(T=6, H=10, W=12), LayerSpec(0, (1, 10, 12)), 128, 2),
     ("many_blocks_3d", "l3d_55k", dict(T=8, H=12, W=32), LayerSpec(2, (2, 2, 2)), 64, 2),
+    # two batch entries (head groups g = b*Hh + h of both)
+    ("batch2_3d", "l3d_55k", dict(T=4, H=12, W=16, batch=2), LayerSpec(2, (4, 6, 8)), 128, 2),
     # the block-count limit: 1024 blocks of 8 tokens, 32 mask words per token
     ("max_blocks_3d", "l3d_55k", dict(T=8, H=32, W=32), LayerSpec(2, (2, 2, 2)), 64, 1),
 ]
@@ -61,10 +63,11 @@ def _setup(case, tau=0.25):
     name, cfgname, lat, spec, hd, heads = case
     cfg = dict(CONFIGS[cfgname])
     cfg.update(lat)
-    over = dict(lat, heads=heads, head_dim=hd, batch=1)
+    batch = lat.get("batch", 1)
+    over = dict(lat, heads=heads, head_dim=hd, batch=batch)
     inp = make_layer_inputs(cfgname, 0, backward=True, shape_override=over, dtype="bf16")
-    p = Problem(1, heads, hd, cfg["T"], cfg["H"], cfg["W"], spec.layer_idx, tuple(spec.block),
-                torch.bfloat16, torch.float32)
+    p = Problem(batch, heads, hd, cfg["T"], cfg["H"], cfg["W"], spec.layer_idx,
+                tuple(spec.block), torch.bfloat16, torch.float32)
     mem = oracle.block_members(p.T, p.H, p.W, p.block)
     blk = oracle.block_of_token(mem, p.L)
     print(f"[token case {name}] L={p.L} N_b={mem.shape[0]} tau={tau}", flush=True)
@@ -81,12 +84,15 @@ def test_token_selection_matches_oracle(case):
     _, kp = vmoba_partition_pool(p, q, k)
     sel = vmoba_select_tokens(p, q, kp, 0.25)
     torch.cuda.synchronize()
-    gm = bits_to_bool(sel.token_mask, nb)             # [G, L, nb]
+    gm = bits_to_bool(sel.token_mask, nb)             # [G, L, nb], g = b*Hh + h
+    G = p.groups
+    om = mask.reshape(G, p.L, nb)
+    osh = shat.reshape(G, p.L, nb)
     bad = exempt = 0
-    for h in range(p.heads):
-        v = stats[h]["v"]
-        diff = gm[h] != mask[0, h]
-        near = np.abs(shat[0, h] - v) <= WINDOW * v
+    for g in range(G):
+        v = stats[g]["v"]
+        diff = gm[g] != om[g]
+        near = np.abs(osh[g] - v) <= WINDOW * v
         bad += int((diff & ~near).sum())
         exempt += int((diff & near).sum())
     print(f"  mismatches {bad}, exempt {exempt}", flush=True)
@@ -97,11 +103,11 @@ def test_token_selection_matches_oracle(case):
     assert (masks_from_csr(sel.row_ptr, sel.col_idx, nb) == union).all()
     assert (masks_from_csc(sel.col_ptr, sel.row_idx, nb) == union).all()
     hs = sel.head_stats.cpu().numpy()
-    for h in range(p.heads):
-        assert hs[h, 1] == gm[h].sum()
-        assert abs(hs[h, 0] - stats[h]["k"]) <= max(2, exempt)
-        assert abs(hs[h, 2] - stats[h]["mass"]) <= 1e-4
-        assert abs(hs[h, 3] - stats[h]["v"]) <= 1e-4 * stats[h]["v"] + 1e-9
+    for g in range(G):
+        assert hs[g, 1] == gm[g].sum()
+        assert abs(hs[g, 0] - stats[g]["k"]) <= max(2, exempt)
+        assert abs(hs[g, 2] - stats[g]["mass"]) <= 1e-4
+        assert abs(hs[g, 3] - stats[g]["v"]) <= 1e-4 * stats[g]["v"] + 1e-9
 
 
 def _token_attention(case, mask, blk, mem, p, inp, tm_override=None):
@@ -109,7 +115,7 @@ def _token_attention(case, mask, blk, mem, p, inp, tm_override=None):
     tm = mask if tm_override is None else tm_override
     union = otok.union_block_mask(tm, mem)
     rp, ci, cp, ri = csr_to_device(union, DEV)
-    bits = bool_to_bits(tm[0]).to(DEV)
+    bits = bool_to_bits(tm.reshape(-1, tm.shape[2], tm.shape[3])).to(DEV)
     q, k, v, do = (inp[x].to(DEV) for x in ("q", "k", "v", "do"))
     o, lse = vmoba_token_attn_fwd(p, q, k, v, rp, ci, bits)
     dq, dk, dv = vmoba_token_attn_bwd(p, q, k, v, o, lse, do, rp, ci, cp, ri, bits)
