@@ -104,6 +104,7 @@ def _kernel_source_hash(kernel):
     import hashlib
     src = {"attn_fwd_bf16_kernel": "attn_fwd.hip", "attn_fwd16_bf16_kernel": "attn_fwd.hip",
            "attn_bwd_dkdv_bf16_kernel": "attn_bwd.hip",
+           "attn_bwd_dkdv16_bf16_kernel": "attn_bwd.hip",
            "attn_bwd_dq_bf16_kernel": "attn_bwd.hip"}[kernel]
     h = hashlib.sha256()
     for fn in (src, "attn_common.h", "device_common.h"):
@@ -139,6 +140,14 @@ def fwd_kernel_name(qlim, head_dim, bf16):
     if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= -(-qlim // 128) * 128:
         return "attn_fwd16_bf16_kernel"
     return "attn_fwd_bf16_kernel"
+
+
+def dkdv_kernel_name(klim, head_dim, bf16):
+    """The dK/dV kernel the library launches: 48 keys per wave (16x16x32 MFMA) at d = 128
+    when 192-key tiles pad no more than 128-key ones."""
+    if bf16 and head_dim == 128 and -(-klim // 192) * 192 <= -(-klim // 128) * 128:
+        return "attn_bwd_dkdv16_bf16_kernel"
+    return "attn_bwd_dkdv_bf16_kernel"
 
 
 def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
@@ -204,7 +213,8 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
     pool_bytes = 2.0 * p.L * p.groups * d * esz + 2.0 * p.groups * nb * d * 4
     select_bytes = 2.0 * p.groups * nb * d * 4 + 6.0 * p.groups * nb * nb * 4
     kernel_names = {"fwd": fwd_kernel_name(S, d, dtype == torch.bfloat16),
-                    "dkdv": "attn_bwd_dkdv_bf16_kernel", "dq": "attn_bwd_dq_bf16_kernel"}
+                    "dkdv": dkdv_kernel_name(S, d, dtype == torch.bfloat16),
+                    "dq": "attn_bwd_dq_bf16_kernel"}
 
     dense = None
     if dense_reps > 0:

@@ -350,6 +350,324 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 }
 
 // ---------------------------------------------------------------------------------
+// dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16: each wave owns 48 keys (three 16-key
+// sub-tiles) of one key block, so a workgroup covers 192 keys (a whole 192-token block)
+// and every Q / dO fragment read from LDS feeds three products.  The accumulators of 48
+// keys (dK^T and dV^T, 192 registers per lane) need one wave per SIMD.
+//
+// Per 32-query tile and wave:
+//   S = Q K^T and dP = dO V^T as 2 query sub-tiles x 3 key sub-tiles x 4 d-steps (A = Q or
+//   dO rows from LDS, B = this wave's K or V columns in registers); the accumulator gives
+//   lane l the key l % 16 of each key sub-tile and queries 4*(l/16) + 0..3 of each query
+//   sub-tile;
+//   P = exp(S / sqrt(d) - lse), dS = P (dP - delta), packed with their k order permuted to
+//   the accumulator layout (k position 8g + e is query 4g + e for e < 4 and 16 + 4g + e - 4
+//   otherwise): they are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//   operands (dO^T, Q^T) come from two transposing reads each that follow the same
+//   permutation.
+//
+// LDS tiles: row r holds one query (256 bytes, 16 chunks of 16 bytes), chunk c at position
+// c ^ (2 (r & 7) | ((r >> 3) & 1)).  Both access patterns are conflict-free with it: a row
+// read takes one chunk column of 16 consecutive rows (16 distinct positions), and a
+// transposing read takes 8 rows x 32 bytes per half-wave (8 distinct chunk pairs).
+__device__ __forceinline__ int swz16(int r) { return (2 * (r & 7)) | ((r >> 3) & 1); }
+
+template <bool DENSE, bool TAB, typename GT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
+  constexpr int D = 128, NW = 4, NT = 256;
+  constexpr int KS = 3;                      // key sub-tiles per wave
+  constexpr int KW = 16 * KS;                // keys per wave
+  constexpr int KWG = NW * KW;               // keys per workgroup
+  constexpr int QT = 32;                     // queries per tile
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = QT * ROWB;            // bytes of one Q or dO tile
+  constexpr int LPW = QT / (NW * 4);         // load instructions per wave per tensor
+  constexpr int NS = 4;                      // pipeline stages
+  constexpr int PER_TILE = 2 * LPW + 1;      // loads per wave per tile
+  // per stage: Q tile, dO tile, then four 64-float slots: LSE (waves 0, 2), delta (1, 3);
+  // every wave loads one slot so that all waves count the same loads per tile
+  constexpr int STAGE = 2 * TILE + 4 * 64 * 4;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[STAGE];
+  __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
+  __shared__ int32_t scratch[NW];
+  auto stage = [&](auto Ic) -> unsigned char* {
+    constexpr int I = decltype(Ic)::value % NS;
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
+  };
+
+  const Geom& g = a.g;
+  const int nrow = DENSE ? 1 : g.Nb;
+  int bid = xcd_item(blockIdx.x, g.B * g.Hh, nrow * a.tiles);
+  if (bid < 0) return;
+  const int kt = bid % a.tiles;
+  bid /= a.tiles;
+  const int jblk = bid % nrow;
+  const int grp = bid / nrow;
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
+  GT* __restrict__ dK = static_cast<GT*>(a.dk);
+  GT* __restrict__ dV = static_cast<GT*>(a.dv);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * D) * 2u;   // < 2^32 (validated)
+  const BufRes rQ = buffer_res(Q, tbytes), rO = buffer_res(dO, tbytes);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int g16 = lane >> 4, i16 = lane & 15;
+
+  int nq;
+  if constexpr (DENSE) {
+    nq = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.col_ptr, grp, jblk, &start, &len);
+    const int kept = compact_list<NT>(a.row_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, rows_l, scratch);
+    for (int i = tid; i < kept; i += NT) rows_l[i] = block_base(g, uint32_t(rows_l[i]));
+    if (kept == 0 && tid == 0) rows_l[0] = 0;   // token 0: address of an empty stream
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+    __syncthreads();
+    nq = kept * g.S;
+  }
+  const int ntiles = (nq + QT - 1) / QT;
+
+  // this wave's keys: K and V columns (B operands) in registers
+  const int klim = DENSE ? g.L : g.S;
+  const int kbase = kt * KWG + w * KW;
+  const bool wave_busy = kbase < klim;   // otherwise: loads and barriers only
+  auto key_token = [&](int ks) -> int32_t {
+    const int rk = kbase + ks * 16 + i16;
+    const int rkc = rk < klim ? rk : 0;
+    return DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
+  };
+  bf16x8 kf[KS][D / 32], vf[KS][D / 32];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int32_t koff = row_offset(g, grp, key_token(ks));
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) {
+      kf[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + koff + s * 32 + g16 * 8));
+      vf[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(V + koff + s * 32 + g16 * 8));
+    }
+  }
+  f32x4 dkacc[D / 16][KS], dvacc[D / 16][KS];
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      dkacc[ds][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dvacc[ds][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // query stream loader: one instruction moves 4 rows; lane L fills row L/16 at chunk
+  // position L % 16 (logical chunk (L % 16) ^ swz16(row))
+  const float* lse_g = a.lse + size_t(grp) * g.L;
+  const float* dl_g = a.delta + size_t(grp) * g.L;
+  const BufRes rL = buffer_res(lse_g, uint32_t(g.L) * 4u);
+  const BufRes rD = buffer_res(dl_g, uint32_t(g.L) * 4u);
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  const int plast = max(nq - 1, 0);   // positions past the end repeat the last query
+  int chunk[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int r = w * (QT / NW) + i * 4 + g16;
+    chunk[i] = (i16 ^ swz16(r)) * 8;
+  }
+  auto qtoken = [&](int p) -> int32_t {
+    if constexpr (DENSE) {
+      return p;
+    } else {
+      const uint32_t bi = fd_div(uint32_t(p), g.div_S);
+      const uint32_t r = uint32_t(p) - bi * uint32_t(g.S);
+      return rows_l[bi] + (TAB ? offtab[r] : block_offset(g, r));
+    }
+  };
+  // element offsets of this lane's Q/dO rows of tile t, and the token of its LSE/delta
+  auto tile_offsets = [&](int t, int32_t (&o)[LPW], int32_t& xl) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i)
+      o[i] = gbase + qtoken(min(t * QT + w * (QT / NW) + i * 4 + g16, plast)) * hstride;
+    xl = qtoken(min(t * QT + (lane & 31), plast));
+  };
+  auto issue_offsets = [&](const int32_t (&o)[LPW], int32_t xl, unsigned char* sb) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int dst = (wu * (QT / NW) + i * 4) * ROWB;
+      load_to_lds16(rQ, 2u * uint32_t(o[i] + chunk[i]), sb + dst);
+      load_to_lds16(rO, 2u * uint32_t(o[i] + chunk[i]), sb + TILE + dst);
+    }
+    // scalar branch: the descriptor stays uniform
+    if (wu & 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
+    else load_to_lds4(rL, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
+  };
+  auto issue_tile = [&](int t, unsigned char* sb) {
+    int32_t o[LPW], xl;
+    tile_offsets(t, o, xl);
+    issue_offsets(o, xl, sb);
+  };
+
+  // LDS read offsets of this lane: row reads take row 16 qs + l%16, chunk 4 s + l/16; the
+  // transposing reads name row 4 (l/16) + (l%16)/4 (+16) and 8 bytes of chunk 2 ds + ((l%4)/2)
+  const int rrd = i16 * ROWB;
+  const int rsw = swz16(i16);
+  const int trow = 4 * g16 + (i16 >> 2);
+  const int trd = trow * ROWB + 8 * (i16 & 1);
+  const int tsw = swz16(trow);
+  const int tc = (i16 & 3) >> 1;
+  const float c2 = a.scale_log2;
+
+  auto compute = [&](const unsigned char* sb, int t) __attribute__((always_inline)) {
+    const unsigned char* qb = sb;
+    const unsigned char* ob = sb + TILE;
+    const float* lse_s = reinterpret_cast<const float*>(sb + 2 * TILE);
+    const float* dl_s = lse_s + 64;
+    f32x4 sacc[2][KS], pacc[2][KS];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int o = qs * 16 * ROWB + rrd + 16 * ((4 * s + g16) ^ rsw);
+        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + o));
+        const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(ob + o));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sacc[qs][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[ks][s], sacc[qs][ks],
+                                                                 0, 0, 0);
+          pacc[qs][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[ks][s], pacc[qs][ks],
+                                                                 0, 0, 0);
+        }
+      }
+    // P and dS; queries 16 qs + 4 (l/16) + i of the tile, key l%16 of each sub-tile
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qs * 16 + 4 * g16);
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_s + qs * 16 + 4 * g16);
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qs][ks][i], c2, -lv[i]));
+          sacc[qs][ks][i] = pv;
+          pacc[qs][ks][i] = pv * (pacc[qs][ks][i] - dv4[i]);
+        }
+    }
+    if (t * QT + QT > nq) {   // ragged last tile (uniform branch): no P, dS past the end
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t * QT + qs * 16 + 4 * g16 + i >= nq) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              sacc[qs][ks][i] = 0.f;
+              pacc[qs][ks][i] = 0.f;
+            }
+          }
+    }
+    bf16x8 pb[KS], sbf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      pb[ks] = as_bf16x8(u32x4{pack_bf16x2(sacc[0][ks][0], sacc[0][ks][1]),
+                               pack_bf16x2(sacc[0][ks][2], sacc[0][ks][3]),
+                               pack_bf16x2(sacc[1][ks][0], sacc[1][ks][1]),
+                               pack_bf16x2(sacc[1][ks][2], sacc[1][ks][3])});
+      sbf[ks] = as_bf16x8(u32x4{pack_bf16x2(pacc[0][ks][0], pacc[0][ks][1]),
+                                pack_bf16x2(pacc[0][ks][2], pacc[0][ks][3]),
+                                pack_bf16x2(pacc[1][ks][0], pacc[1][ks][1]),
+                                pack_bf16x2(pacc[1][ks][2], pacc[1][ks][3])});
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, one 16-d tile at a time
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int o = trd + 16 * ((2 * ds + tc) ^ tsw);
+      const u32x2 olo = lds_read_tr16(ob + o), ohi = lds_read_tr16(ob + o + 16 * ROWB);
+      const u32x2 qlo = lds_read_tr16(qb + o), qhi = lds_read_tr16(qb + o + 16 * ROWB);
+      const bf16x8 ot = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+      const bf16x8 qt2 = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        dvacc[ds][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pb[ks], dvacc[ds][ks],
+                                                                0, 0, 0);
+        dkacc[ds][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt2, sbf[ks], dkacc[ds][ks],
+                                                                0, 0, 0);
+      }
+    }
+  };
+
+  // pipeline: tile t in stage t % 4, tiles t+1, t+2 in flight while t is computed
+  int32_t noff[LPW], nxl;
+  auto step = [&](auto STc, int t) {
+    constexpr int ST = decltype(STc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lds<(NS - 2) * PER_TILE>();   // this wave's loads of tile t have landed
+    pipeline_barrier();
+    issue_offsets(noff, nxl, stage(std::integral_constant<int, ST + NS - 1>{}));
+    tile_offsets(t + NS, noff, nxl);
+    if (wave_busy) compute(stage(STc), t);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  issue_tile(0, stage0);
+  issue_tile(1, stage1);
+  issue_tile(2, stage2);
+  tile_offsets(NS - 1, noff, nxl);
+  int t = 0;
+  for (; t + NS <= ntiles; t += NS) {
+    step(I0{}, t);
+    step(I1{}, t + 1);
+    step(I2{}, t + 2);
+    step(I3{}, t + 3);
+  }
+  if (t < ntiles) step(I0{}, t);
+  if (t + 1 < ntiles) step(I1{}, t + 1);
+  if (t + 2 < ntiles) step(I2{}, t + 2);
+  // the loads of the tiles past the end must land before the LDS is released
+  wait_vmcnt_lds<0>();
+
+  // dK^T, dV^T tiles: lane l holds key l%16 of sub-tile ks, d = 16 ds + 4 (l/16) + 0..3
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (kbase + ks * 16 + i16 < klim) {
+      const int32_t koff = row_offset(g, grp, key_token(ks));
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds) {
+        const int d0 = ds * 16 + 4 * g16;
+        const float sc = a.scale;
+        store4(dK + koff + d0, dkacc[ds][ks][0] * sc, dkacc[ds][ks][1] * sc,
+               dkacc[ds][ks][2] * sc, dkacc[ds][ks][3] * sc);
+        store4(dV + koff + d0, dvacc[ds][ks][0], dvacc[ds][ks][1], dvacc[ds][ks][2],
+               dvacc[ds][ks][3]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
 // TOK: token-granular selection, as in the forward (list-position mask of the query).
 template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT, bool TOK = false>
@@ -795,11 +1113,31 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
                                          static_cast<const T*>(dout), delta);
 }
 
+template <bool DENSE, typename GT>
+static void launch_dkdv16_bf16(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + 191) / 192;
+  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_bwd_dkdv16_bf16_kernel<DENSE, !DENSE, GT><<<grid, 256, 0, s>>>(a);
+  else
+    attn_bwd_dkdv16_bf16_kernel<DENSE, false, GT><<<grid, 256, 0, s>>>(a);
+}
+
 template <int D, bool DENSE, typename GT, bool TOK = false>
 static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
+  if constexpr (D == 128 && !TOK) {
+    // 48 keys per wave when 192-key tiles pad a block no more than 128-key ones
+    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
+      launch_dkdv16_bf16<DENSE, GT>(a, s);
+      return;
+    }
+  }
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
   const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
