@@ -367,10 +367,12 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 //   permutation.
 //
 // LDS tiles: row r holds one query (256 bytes, 16 chunks of 16 bytes), chunk c at position
-// c ^ (2 (r & 7) | ((r >> 3) & 1)).  Both access patterns are conflict-free with it: a row
-// read takes one chunk column of 16 consecutive rows (16 distinct positions), and a
-// transposing read takes 8 rows x 32 bytes per half-wave (8 distinct chunk pairs).
-__device__ __forceinline__ int swz16(int r) { return (2 * (r & 7)) | ((r >> 3) & 1); }
+// c ^ 2 (r & 7).  Both access patterns run free of bank conflicts with it (the bank-conflict
+// counter reads zero for each pattern in isolation on gfx950): row reads, 16 bytes a lane
+// from one chunk column of 16 consecutive rows, and transposing reads, 8 bytes a lane from
+// 4 rows x 32 bytes per 16 lanes.  The position sets that look distinct on paper are not
+// enough: c ^ (2 (r & 7) | (r >> 3)) halves the rate of the row reads.
+__device__ __forceinline__ int swz16(int r) { return 2 * (r & 7); }
 
 template <bool DENSE, bool TAB, typename GT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
