@@ -96,13 +96,20 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
-  const int nrow = DENSE ? 1 : g.Nb;
-  int bid = xcd_item(blockIdx.x, g.B * g.Hh, nrow * a.tiles);
-  if (bid < 0) return;
-  const int kt = bid % a.tiles;
-  bid /= a.tiles;
-  const int jblk = bid % nrow;
-  const int grp = bid / nrow;
+  int grp, jblk, kt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    kt = bid % a.tiles;
+    jblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.col_ptr, a.tiles, a.ordered != 0, rows_l, scratch, &it)) return;
+    grp = it.grp;
+    jblk = it.blk;
+    kt = it.tile;
+  }
 
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
@@ -407,13 +414,20 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
   };
 
   const Geom& g = a.g;
-  const int nrow = DENSE ? 1 : g.Nb;
-  int bid = xcd_item(blockIdx.x, g.B * g.Hh, nrow * a.tiles);
-  if (bid < 0) return;
-  const int kt = bid % a.tiles;
-  bid /= a.tiles;
-  const int jblk = bid % nrow;
-  const int grp = bid / nrow;
+  int grp, jblk, kt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    kt = bid % a.tiles;
+    jblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.col_ptr, a.tiles, a.ordered != 0, rows_l, scratch, &it)) return;
+    grp = it.grp;
+    jblk = it.blk;
+    kt = it.tile;
+  }
 
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
@@ -691,13 +705,20 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   __shared__ int32_t scratch[NW];
 
   const Geom& g = a.g;
-  const int rows = DENSE ? 1 : g.Nb;
-  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
-  if (bid < 0) return;
-  const int qt = bid % a.tiles;
-  bid /= a.tiles;
-  const int iblk = bid % rows;
-  const int grp = bid / rows;
+  int grp, iblk, qt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    qt = bid % a.tiles;
+    iblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.row_ptr, a.tiles, a.ordered != 0, cols, scratch, &it)) return;
+    grp = it.grp;
+    iblk = it.blk;
+    qt = it.tile;
+  }
 
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
@@ -1121,7 +1142,7 @@ static void launch_dkdv16_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 191) / 192;
-  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dkdv16_bf16_kernel<DENSE, !DENSE, GT><<<grid, 256, 0, s>>>(a);
   else
@@ -1142,7 +1163,7 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   }
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
-  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, !DENSE, GT, TOK><<<grid, NWK * 64, 0, s>>>(a);
   else
@@ -1156,7 +1177,7 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;
-  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK><<<grid, 256, 0, s>>>(a);
   else

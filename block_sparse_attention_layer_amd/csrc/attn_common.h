@@ -38,6 +38,8 @@ struct AttnParams {
   const uint32_t* tokmask;
   const uint32_t* posmask;
   int32_t mwords;
+  // sparse launches: take each head group's lists longest first (sparse_item)
+  int32_t ordered;
 };
 
 // A query token's row of the list-position mask (bit li of word li >> 5: the li-th key
@@ -154,6 +156,80 @@ __device__ __forceinline__ void list_range(const Geom& g, const int32_t* ptr, in
   e = min(max(e, s), min(cap, s + g.Nb));
   *start = s;
   *len = e - s;
+}
+
+// Work item of a sparse attention workgroup: head group, block (whose row or column
+// list it walks) and tile of that block.  Workgroups start roughly in launch order and
+// their cost grows with the length of their list, which varies several-fold between the
+// blocks of a head under a global selection; taken in block order, the longest lists
+// can start last and leave a tail in which most of the chip idles.  With `ordered`, the
+// blocks of each head group are taken longest list first (ties by ascending block
+// index), and launch index b goes to XCD b % 8, which takes the sorted positions x, x+8,
+// x+16, ... of the current head group, each with all of its tiles in a row.  Head
+// groups still follow each other (one or two heads' K/V in the shared cache at a time).
+// The rank of every list is found inside the workgroup: list lengths into `lds` (room
+// for N_b rounded up to 4), then a count over all pairs, O(N_b^2 / NT) steps a thread.
+struct SparseItem {
+  int grp, blk, tile;
+};
+
+inline int sparse_grid(int groups, int nb, int tiles) {
+  return groups * kXcds * ((nb + kXcds - 1) / kXcds) * tiles;
+}
+
+// Lists are ranked inside the workgroups only up to this many blocks a head: the count
+// over all pairs costs O(N_b^2 / NT) per workgroup, while the work of a workgroup shrinks
+// as N_b grows (smaller blocks).
+constexpr int kOrderedMaxBlocks = 512;
+
+// Grid of a bf16 attention launch (a.tiles set); sets a.ordered for sparse launches.
+template <bool DENSE>
+inline int launch_grid(AttnParams& a, int rows) {
+  if (DENSE) return xcd_grid(a.g.B * a.g.Hh, rows * a.tiles);
+  a.ordered = a.g.Nb <= kOrderedMaxBlocks;
+  return sparse_grid(a.g.B * a.g.Hh, a.g.Nb, a.tiles);
+}
+
+// Returns false for the padding workgroups of the grid (the whole workgroup alike).
+template <int NT>
+__device__ bool sparse_item(const Geom& g, const int32_t* ptr, int tiles, bool ordered,
+                            int32_t* lds, int32_t* pick, SparseItem* it) {
+  const int nb = g.Nb;
+  const int chunk = ((nb + kXcds - 1) / kXcds) * tiles;
+  const int k = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
+  const int grp = k / chunk, r = k - grp * chunk;
+  const int pos = (r / tiles) * kXcds + x;
+  if (grp >= g.B * g.Hh || pos >= nb) return false;
+  it->grp = grp;
+  it->tile = r % tiles;
+  it->blk = pos;
+  if (!ordered) return true;
+  const int nb4 = (nb + 3) & ~3;
+  for (int i = threadIdx.x; i < nb4; i += NT) {
+    int len = -1;   // padding: below every real length
+    if (i < nb) {
+      int s, l;
+      list_range(g, ptr, grp, i, &s, &l);
+      len = l;
+    }
+    lds[i] = len;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nb; j += NT) {
+    const int lj = lds[j];
+    int rank = 0;
+    for (int i = 0; i < nb4; i += 4) {
+      const int4 l4 = *reinterpret_cast<const int4*>(lds + i);
+      rank += (l4.x > lj) + (l4.y > lj) + (l4.z > lj) + (l4.w > lj);
+      rank += (l4.x == lj && i < j) + (l4.y == lj && i + 1 < j) + (l4.z == lj && i + 2 < j) +
+              (l4.w == lj && i + 3 < j);
+    }
+    if (rank == pos) *pick = j;   // ranks are a permutation: exactly one thread writes
+  }
+  __syncthreads();
+  it->blk = *pick;
+  __syncthreads();   // lds and pick are the caller's to reuse
+  return true;
 }
 
 // ---------------------------------------------------------------------------------

@@ -58,13 +58,20 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   };
 
   const Geom& g = a.g;
-  const int rows = DENSE ? 1 : g.Nb;
-  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
-  if (bid < 0) return;
-  const int qt = bid % a.tiles;
-  bid /= a.tiles;
-  const int iblk = bid % rows;
-  const int grp = bid / rows;
+  int grp, iblk, qt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    qt = bid % a.tiles;
+    iblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.row_ptr, a.tiles, a.ordered != 0, cols, scratch, &it)) return;
+    grp = it.grp;
+    iblk = it.blk;
+    qt = it.tile;
+  }
 
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
@@ -409,13 +416,20 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   };
 
   const Geom& g = a.g;
-  const int rows = DENSE ? 1 : g.Nb;
-  int bid = xcd_item(blockIdx.x, g.B * g.Hh, rows * a.tiles);
-  if (bid < 0) return;
-  const int qt = bid % a.tiles;
-  bid /= a.tiles;
-  const int iblk = bid % rows;
-  const int grp = bid / rows;
+  int grp, iblk, qt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    qt = bid % a.tiles;
+    iblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.row_ptr, a.tiles, a.ordered != 0, cols, scratch, &it)) return;
+    grp = it.grp;
+    iblk = it.blk;
+    qt = it.tile;
+  }
 
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
@@ -762,7 +776,7 @@ static void launch_fwd_bf16(AttnParams& a, hipStream_t s) {
   const int qlim = DENSE ? g.L : g.S;
   a.tiles = (qlim + NW * 32 - 1) / (NW * 32);
   const int rows = DENSE ? 1 : g.Nb;
-  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
     attn_fwd_bf16_kernel<D, NW, KSUB, NS, DENSE, !DENSE, TOK><<<grid, NW * 64, 0, s>>>(a);
   else
@@ -775,7 +789,7 @@ static void launch_fwd16_bf16(AttnParams& a, hipStream_t s) {
   const int qlim = DENSE ? g.L : g.S;
   a.tiles = (qlim + 64 * M - 1) / (64 * M);
   const int rows = DENSE ? 1 : g.Nb;
-  const int grid = xcd_grid(g.B * g.Hh, rows * a.tiles);
+  const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
     attn_fwd16_bf16_kernel<M, 4, DENSE, !DENSE><<<grid, 256, 0, s>>>(a);
   else
