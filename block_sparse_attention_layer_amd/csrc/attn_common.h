@@ -164,9 +164,11 @@ __device__ __forceinline__ void list_range(const Geom& g, const int32_t* ptr, in
 // blocks of a head under a global selection; taken in block order, the longest lists
 // can start last and leave a tail in which most of the chip idles.  With `ordered`, the
 // blocks of each head group are taken longest list first (ties by ascending block
-// index), and launch index b goes to XCD b % 8, which takes the sorted positions x, x+8,
-// x+16, ... of the current head group, each with all of its tiles in a row.  Head
-// groups still follow each other (one or two heads' K/V in the shared cache at a time).
+// index), and launch index b goes to XCD x = b % 8, which takes the sorted positions
+// p, p+8, p+16, ... of the current head group g, p = (x + g) mod 8, each with all of its
+// tiles in a row (they share their stream in that XCD's L2).  Rotating p with g evens
+// out the XCDs' shares when N_b is not a multiple of 8.  Head groups still follow each
+// other (one or two heads' K/V in the shared cache at a time).
 // The rank of every list is found inside the workgroup: list lengths into `lds` (room
 // for N_b rounded up to 4), then a count over all pairs, O(N_b^2 / NT) steps a thread.
 struct SparseItem {
@@ -198,7 +200,7 @@ __device__ bool sparse_item(const Geom& g, const int32_t* ptr, int tiles, bool o
   const int chunk = ((nb + kXcds - 1) / kXcds) * tiles;
   const int k = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
   const int grp = k / chunk, r = k - grp * chunk;
-  const int pos = (r / tiles) * kXcds + x;
+  const int pos = (r / tiles) * kXcds + ((x + grp) & (kXcds - 1));
   if (grp >= g.B * g.Hh || pos >= nb) return false;
   it->grp = grp;
   it->tile = r % tiles;
