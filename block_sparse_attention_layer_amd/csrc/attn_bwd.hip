@@ -686,7 +686,13 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
 // ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
 // TOK: token-granular selection, as in the forward (list-position mask of the query).
-template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT, bool TOK = false>
+// NS: K/V tile stages.  With 4, step t waits only for this wave's loads of tile t, passes
+// a barrier and refills the stage of tile t-1 with tile t+3 (as the forward does).  With
+// 2 (the TOK instances, whose per-query mask-word loads would interleave with the tile
+// loads on the same counter), the loads of tile t+1 are in flight during tile t and the
+// step ends waiting for all of them.
+template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT, bool TOK = false,
+          int NS = 2>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -698,8 +704,18 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   static_assert(KT % (NW * RPI) == 0, "tile rows split over waves");
   constexpr int TILE = KT * ROWB;
 
+  static_assert(NS == 2 || (NS == 4 && !TOK), "stages");
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[NS > 2 ? 2 * TILE : 1];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[NS > 2 ? 2 * TILE : 1];
+  auto stage = [&](auto Ic) -> unsigned char* {
+    constexpr int I = decltype(Ic)::value % NS;
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
+  };
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];   // block_offset(r), r < S
   __shared__ int32_t scratch[NW];
@@ -807,24 +823,20 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 
   const float c2 = a.scale_log2;
   const int grp16 = lane >> 4, sl = lane & 15;
-  auto step = [&](auto STc, int t) {
-    constexpr int ST = decltype(STc)::value;
-    __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
-    unsigned char* const cur = ST ? stage1 : stage0;
-    unsigned char* const nxt = ST ? stage0 : stage1;
-    // the two mask words of this tile, loaded before the next tile's loads are issued so
-    // that waiting for them does not wait for those
-    uint32_t pw0 = 0u, pw1 = 0u;
-    if constexpr (TOK) {
-      const int wi = int(fd_div(uint32_t(t * KT), g.div_S)) >> 5;
-      pw0 = wi < a.mwords ? a.posmask[pmrow + wi] : 0u;
-      pw1 = wi + 1 < a.mwords ? a.posmask[pmrow + wi + 1] : 0u;
-    }
-    if (t + 1 < ntiles) {
-      issue_offsets(noff, nxt);
-      tile_offsets(t + 2, noff);
-    }
-    if (wave_busy) {
+  // lane offsets of the K^T reads of key sub-tile 0 (the swizzle repeats every 16 rows,
+  // so sub-tile ks adds 16 ks rows): key 4 (l/32) + (l%16)/4 (+8 for the upper half),
+  // chunk 4 dt + 2 ((l/16) % 2) + (l%4)/2, 8 bytes at (l%2) * 8
+  int trlo[D / 32], trhi[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int key0 = 4 * half + (sl >> 2);
+    const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
+    const int bo = (sl & 1) * 8;
+    trlo[dt] = tile_off<D>(key0, c) + bo;
+    trhi[dt] = tile_off<D>(key0 + 8, c) + bo;
+  }
+  auto compute = [&](const unsigned char* cur, int t, uint32_t pw0, uint32_t pw1)
+      __attribute__((always_inline)) {
     // token-granular selection: which of this lane's keys its query selected, worked out
     // before the products take the registers (one bit per key)
     uint32_t keepbits = ~0u;
@@ -885,15 +897,21 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
         }
     }
     bf16x8 kt[2 * KSUB][D / 32];   // K^T fragments of dQ^T += K^T dS^T (transposing reads)
+    // this tile's copies of the lane offsets: opaque, so that the stage base is added at
+    // the read (immediate offset) instead of hoisting one address per stage and offset
+    int tl[D / 32], th[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      tl[dt] = trlo[dt];
+      th[dt] = trhi[dt];
+      asm volatile("" : "+v"(tl[dt]), "+v"(th[dt]));
+    }
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
-      const int key0 = ks * 16 + 4 * half + (sl >> 2);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int c = dt * 4 + 2 * (grp16 & 1) + ((sl & 3) >> 1);
-        const int bo = (sl & 1) * 8;
-        const u32x2 lo = lds_read_tr16(kb + tile_off<D>(key0, c) + bo);
-        const u32x2 hi = lds_read_tr16(kb + tile_off<D>(key0 + 8, c) + bo);
+        const u32x2 lo = lds_read_tr16(kb + tl[dt] + ks * 16 * ROWB);
+        const u32x2 hi = lds_read_tr16(kb + th[dt] + ks * 16 * ROWB);
         kt[ks][dt] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
     }
@@ -931,24 +949,77 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
       for (int dt = 0; dt < D / 32; ++dt)
         dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks][dt], sbf, dqacc[dt], 0, 0, 0);
     }
-    }
-    wait_lds_loads();
-    __syncthreads();
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  tile_offsets(0, noff);
-  if (ntiles > 0) issue_offsets(noff, stage0);
-  tile_offsets(1, noff);
-  wait_lds_loads();
-  __syncthreads();
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(S0{}, t);
-    step(S1{}, t + 1);
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if constexpr (NS == 2) {
+    auto step = [&](auto STc, int t) {
+      constexpr int ST = decltype(STc)::value;
+      __builtin_amdgcn_sched_barrier(0);   // keep the steps from being interleaved
+      unsigned char* const cur = ST ? stage1 : stage0;
+      unsigned char* const nxt = ST ? stage0 : stage1;
+      // the two mask words of this tile, loaded before the next tile's loads are issued
+      // so that waiting for them does not wait for those
+      uint32_t pw0 = 0u, pw1 = 0u;
+      if constexpr (TOK) {
+        const int wi = int(fd_div(uint32_t(t * KT), g.div_S)) >> 5;
+        pw0 = wi < a.mwords ? a.posmask[pmrow + wi] : 0u;
+        pw1 = wi + 1 < a.mwords ? a.posmask[pmrow + wi + 1] : 0u;
+      }
+      if (t + 1 < ntiles) {
+        issue_offsets(noff, nxt);
+        tile_offsets(t + 2, noff);
+      }
+      if (wave_busy) compute(cur, t, pw0, pw1);
+      wait_lds_loads();
+      __syncthreads();
+    };
+    tile_offsets(0, noff);
+    if (ntiles > 0) issue_offsets(noff, stage0);
+    tile_offsets(1, noff);
+    wait_lds_loads();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(S0{}, t);
+      step(S1{}, t + 1);
+    }
+    if (t < ntiles) step(S0{}, t);
+  } else {
+    // tiles are loaded unconditionally, one a step; positions past the end repeat the
+    // last key and are never used
+    constexpr int PER_TILE = 2 * LPW;   // loads per wave per tile
+    auto step = [&](auto STc, int t) {
+      constexpr int ST = decltype(STc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lds<(NS - 2) * PER_TILE>();   // this wave's loads of tile t have landed
+      pipeline_barrier();
+      issue_offsets(noff, stage(std::integral_constant<int, ST + NS - 1>{}));
+      tile_offsets(t + NS, noff);
+      if (wave_busy) compute(stage(STc), t, 0u, 0u);
+    };
+    tile_offsets(0, noff);
+    issue_offsets(noff, stage0);
+    tile_offsets(1, noff);
+    issue_offsets(noff, stage1);
+    tile_offsets(2, noff);
+    issue_offsets(noff, stage2);
+    tile_offsets(3, noff);
+    int t = 0;
+    for (; t + NS <= ntiles; t += NS) {
+      step(S0{}, t);
+      step(S1{}, t + 1);
+      step(S2{}, t + 2);
+      step(S3{}, t + 3);
+    }
+    if (t < ntiles) step(S0{}, t);
+    if (t + 1 < ntiles) step(S1{}, t + 1);
+    if (t + 2 < ntiles) step(S2{}, t + 2);
+    wait_vmcnt_lds<0>();   // the loads past the end land before the LDS is released
   }
-  if (t < ntiles) step(S0{}, t);
   if (qvalid) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -1178,10 +1249,11 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;
   const int grid = launch_grid<DENSE>(a, rows);
+  constexpr int NS = TOK ? 2 : 4;
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK, NS><<<grid, 256, 0, s>>>(a);
   else
-    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT, TOK><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT, TOK, NS><<<grid, 256, 0, s>>>(a);
 }
 
 template <int D, bool DENSE>
