@@ -33,6 +33,11 @@ CASES = [
     ("small1d_120", "l1d_32k", dict(T=6, H=10, W=12), LayerSpec(0, (1, 10, 12)), 0.25, "bf16", 128, 1),
     ("small3d_d64_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.5, "bf16", 64, 2),
     ("small3d_fp32", "l3d_55k", dict(T=4, H=12, W=16), LayerSpec(2, (2, 6, 8)), 0.3, "fp32", 128, 1),
+    # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and dK/dV
+    # kernels, three 128-query tiles in dQ, and a block count that is no multiple of 8
+    ("tiles2_3d_384", "l3d_55k", dict(T=8, H=36, W=16), LayerSpec(2, (4, 12, 8)), 0.6, "bf16", 128, 1),
+    # 576 blocks of 8: above the block count up to which launches rank the lists
+    ("unranked_576_blocks", "l3d_55k", dict(T=8, H=18, W=32), LayerSpec(2, (2, 2, 2)), 0.97, "bf16", 128, 1),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -87,7 +92,13 @@ def test_selection_matches_oracle(case):
     # normalised scores and per-head statistics
     G = p.groups
     shat = ref["shat"].reshape(G, nb, nb)
-    assert max_err(to_np(sel.norm_scores), shat) <= 1e-6
+    # fp32 scores carry about sqrt(d) 2^-24 of sum |qbar_i kbar_i|, which exp(s - max)
+    # turns into a relative error: 1e-6 absolute plus 3e-5 relative (the means of small
+    # blocks have the largest scores)
+    ns = to_np(sel.norm_scores)
+    ratio = float(np.max(np.abs(ns - shat) / (1e-6 + 3e-5 * np.abs(shat))))
+    print(f"normalised scores: max-abs {max_err(ns, shat):.3g}, max ratio to bound {ratio:.3g}")
+    assert ratio <= 1.0
     hs = sel.head_stats.cpu().numpy()
     for g in range(G):
         st = ref["stats"][g]
