@@ -104,7 +104,7 @@ def _kernel_source_hash(kernel):
     import hashlib
     src = {"attn_fwd_bf16_kernel": "attn_fwd.hip", "attn_fwd16_bf16_kernel": "attn_fwd.hip",
            "attn_bwd_dkdv_bf16_kernel": "attn_bwd.hip",
-           "attn_bwd_dkdv16_bf16_kernel": "attn_bwd.hip",
+           "attn_bwd_dkdv_split_bf16_kernel": "attn_bwd.hip",
            "attn_bwd_dq_bf16_kernel": "attn_bwd.hip"}[kernel]
     h = hashlib.sha256()
     for fn in (src, "attn_common.h", "device_common.h"):
@@ -143,10 +143,11 @@ def fwd_kernel_name(qlim, head_dim, bf16):
 
 
 def dkdv_kernel_name(klim, head_dim, bf16):
-    """The dK/dV kernel the library launches: 48 keys per wave (16x16x32 MFMA) at d = 128
-    when 192-key tiles pad no more than 128-key ones."""
+    """The dK/dV kernel the library launches: 192 keys a workgroup in key groups of 48, each
+    split over two waves (16x16x32 MFMA), at d = 128 when 192-key tiles pad no more than
+    128-key ones."""
     if bf16 and head_dim == 128 and -(-klim // 192) * 192 <= -(-klim // 128) * 128:
-        return "attn_bwd_dkdv16_bf16_kernel"
+        return "attn_bwd_dkdv_split_bf16_kernel"
     return "attn_bwd_dkdv_bf16_kernel"
 
 

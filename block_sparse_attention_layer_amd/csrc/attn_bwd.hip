@@ -357,14 +357,13 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 }
 
 // ---------------------------------------------------------------------------------
-// dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16: each wave owns 48 keys (three 16-key
-// sub-tiles) of one key block, so a workgroup covers 192 keys (a whole 192-token block)
-// and every Q / dO fragment read from LDS feeds three products.  The accumulators of 48
-// keys (dK^T and dV^T, 192 registers per lane) need one wave per SIMD.
+// dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16.  A workgroup covers 192 keys (a whole
+// 192-token block) in four key groups of 48 keys (three 16-key sub-tiles), so every Q /
+// dO fragment a wave reads from LDS feeds three products.
 //
-// Per 32-query tile and wave:
+// Per 32-query tile and key group:
 //   S = Q K^T and dP = dO V^T as 2 query sub-tiles x 3 key sub-tiles x 4 d-steps (A = Q or
-//   dO rows from LDS, B = this wave's K or V columns in registers); the accumulator gives
+//   dO rows from LDS, B = the group's K or V columns in registers); the accumulator gives
 //   lane l the key l % 16 of each key sub-tile and queries 4*(l/16) + 0..3 of each query
 //   sub-tile;
 //   P = exp(S / sqrt(d) - lse), dS = P (dP - delta), packed with their k order permuted to
@@ -372,6 +371,17 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 //   otherwise): they are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
 //   operands (dO^T, Q^T) come from two transposing reads each that follow the same
 //   permutation.
+//
+// The work of a key group is split over two waves on one SIMD (waves kg and kg + 4 of 8):
+//   role P (waves 0-3): S, P, dV^T += dO^T P; writes P (fp32, accumulator layout) to an
+//     LDS exchange buffer;
+//   role dS (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
+//     been published by the step barrier, dS and dK^T += Q^T dS.
+// Each wave holds one accumulator (96 registers a lane) and one of K or V, so two waves
+// fit a SIMD (256 registers each): the SIMD's matrix core alternates between them while
+// each one's vector work (the softmax, or the dS) runs beside the other's products.  One
+// wave holding both accumulators (192 registers) leaves one wave per SIMD, which measured
+// 9 % slower.  The arithmetic of every element is the same either way.
 //
 // LDS tiles: row r holds one query (256 bytes, 16 chunks of 16 bytes), chunk c at position
 // c ^ 2 (r & 7).  Both access patterns run free of bank conflicts with it (the bank-conflict
@@ -381,27 +391,35 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 // enough: c ^ (2 (r & 7) | (r >> 3)) halves the rate of the row reads.
 __device__ __forceinline__ int swz16(int r) { return 2 * (r & 7); }
 
+// Stages: the Q/dO/LSE/delta of tile t are read by role P at step t and by role dS at
+// steps t and t+1, so step t refills the stage of tile t-2 with tile t+2 (four stages;
+// the loads of a tile have two steps to land).  The exchange buffer alternates with the
+// tile's parity: role P writes tile t's half at step t, role dS reads it at step t+1,
+// and role P overwrites it at step t+2, after the barrier that ends step t+1.
 template <bool DENSE, bool TAB, typename GT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
-  constexpr int D = 128, NW = 4, NT = 256;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
+  constexpr int D = 128, NW = 8, NT = 512, NKG = 4;
   constexpr int KS = 3;                      // key sub-tiles per wave
-  constexpr int KW = 16 * KS;                // keys per wave
-  constexpr int KWG = NW * KW;               // keys per workgroup
+  constexpr int KW = 16 * KS;                // keys per key group
+  constexpr int KWG = NKG * KW;              // keys per workgroup
   constexpr int QT = 32;                     // queries per tile
   constexpr int ROWB = D * 2;
   constexpr int TILE = QT * ROWB;            // bytes of one Q or dO tile
   constexpr int LPW = QT / (NW * 4);         // load instructions per wave per tensor
+  static_assert(LPW == 1, "one row group per wave");
   constexpr int NS = 4;                      // pipeline stages
   constexpr int PER_TILE = 2 * LPW + 1;      // loads per wave per tile
-  // per stage: Q tile, dO tile, then four 64-float slots: LSE (waves 0, 2), delta (1, 3);
+  // per stage: Q tile, dO tile, then eight 64-float slots: LSE (even waves), delta (odd);
   // every wave loads one slot so that all waves count the same loads per tile
-  constexpr int STAGE = 2 * TILE + 4 * 64 * 4;
+  constexpr int STAGE = 2 * TILE + NW * 64 * 4;
+  constexpr int XF = 2 * KS * 4 * 64;        // floats of P one key group passes a tile
 
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage3[STAGE];
+  __shared__ __attribute__((aligned(16))) float xbuf[2][NKG][XF];
   __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
@@ -441,6 +459,8 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int kg = wu & (NKG - 1);
+  const bool role_p = wu < NKG;              // wave-uniform
   const int g16 = lane >> 4, i16 = lane & 15;
 
   int nq;
@@ -460,33 +480,30 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
   }
   const int ntiles = (nq + QT - 1) / QT;
 
-  // this wave's keys: K and V columns (B operands) in registers
+  // this wave's keys: K (role P) or V (role dS) columns, the B operands, in registers
   const int klim = DENSE ? g.L : g.S;
-  const int kbase = kt * KWG + w * KW;
+  const int kbase = kt * KWG + kg * KW;
   const bool wave_busy = kbase < klim;   // otherwise: loads and barriers only
   auto key_token = [&](int ks) -> int32_t {
     const int rk = kbase + ks * 16 + i16;
     const int rkc = rk < klim ? rk : 0;
     return DENSE ? rkc : block_base(g, jblk) + block_offset(g, rkc);
   };
-  bf16x8 kf[KS][D / 32], vf[KS][D / 32];
+  const uint16_t* __restrict__ KV = role_p ? K : V;
+  bf16x8 kvf[KS][D / 32];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int32_t koff = row_offset(g, grp, key_token(ks));
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) {
-      kf[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(K + koff + s * 32 + g16 * 8));
-      vf[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(V + koff + s * 32 + g16 * 8));
-    }
+    for (int s = 0; s < D / 32; ++s)
+      kvf[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(KV + koff + s * 32 + g16 * 8));
   }
-  f32x4 dkacc[D / 16][KS], dvacc[D / 16][KS];
+  // dV^T (role P) or dK^T (role dS) of this wave's keys
+  f32x4 acc[D / 16][KS];
 #pragma unroll
   for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      dkacc[ds][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dvacc[ds][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int ks = 0; ks < KS; ++ks) acc[ds][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // query stream loader: one instruction moves 4 rows; lane L fills row L/16 at chunk
   // position L % 16 (logical chunk (L % 16) ^ swz16(row))
@@ -497,12 +514,8 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
   const int32_t hstride = g.Hh * D;
   const int32_t gbase = row_offset(g, grp, 0);
   const int plast = max(nq - 1, 0);   // positions past the end repeat the last query
-  int chunk[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int r = w * (QT / NW) + i * 4 + g16;
-    chunk[i] = (i16 ^ swz16(r)) * 8;
-  }
+  const int lrow = w * (QT / NW) + g16;
+  const int chunk = (i16 ^ swz16(lrow)) * 8;
   auto qtoken = [&](int p) -> int32_t {
     if constexpr (DENSE) {
       return p;
@@ -512,160 +525,210 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
       return rows_l[bi] + (TAB ? offtab[r] : block_offset(g, r));
     }
   };
-  // element offsets of this lane's Q/dO rows of tile t, and the token of its LSE/delta
-  auto tile_offsets = [&](int t, int32_t (&o)[LPW], int32_t& xl) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i)
-      o[i] = gbase + qtoken(min(t * QT + w * (QT / NW) + i * 4 + g16, plast)) * hstride;
+  // element offset of this lane's Q/dO row of tile t, and the token of its LSE/delta
+  auto tile_offsets = [&](int t, int32_t& o, int32_t& xl) {
+    o = gbase + qtoken(min(t * QT + lrow, plast)) * hstride;
     xl = qtoken(min(t * QT + (lane & 31), plast));
   };
-  auto issue_offsets = [&](const int32_t (&o)[LPW], int32_t xl, unsigned char* sb) {
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int dst = (wu * (QT / NW) + i * 4) * ROWB;
-      load_to_lds16(rQ, 2u * uint32_t(o[i] + chunk[i]), sb + dst);
-      load_to_lds16(rO, 2u * uint32_t(o[i] + chunk[i]), sb + TILE + dst);
-    }
+  auto issue_offsets = [&](int32_t o, int32_t xl, unsigned char* sb) {
+    const int dst = wu * (QT / NW) * ROWB;
+    load_to_lds16(rQ, 2u * uint32_t(o + chunk), sb + dst);
+    load_to_lds16(rO, 2u * uint32_t(o + chunk), sb + TILE + dst);
     // scalar branch: the descriptor stays uniform
     if (wu & 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
     else load_to_lds4(rL, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
   };
   auto issue_tile = [&](int t, unsigned char* sb) {
-    int32_t o[LPW], xl;
+    int32_t o, xl;
     tile_offsets(t, o, xl);
     issue_offsets(o, xl, sb);
   };
 
-  // LDS read offsets of this lane: row reads take row 16 qs + l%16, chunk 4 s + l/16; the
-  // transposing reads name row 4 (l/16) + (l%16)/4 (+16) and 8 bytes of chunk 2 ds + ((l%4)/2)
-  const int rrd = i16 * ROWB;
-  const int rsw = swz16(i16);
-  const int trow = 4 * g16 + (i16 >> 2);
-  const int trd = trow * ROWB + 8 * (i16 & 1);
-  const int tsw = swz16(trow);
-  const int tc = (i16 & 3) >> 1;
+  // LDS read offsets of this lane: row reads of d-step s (query sub-tile 0), transposing
+  // reads of d-tile ds
+  int roff[D / 32], toff[D / 16];
+  {
+    const int rrd = i16 * ROWB;
+    const int rsw = swz16(i16);
+    const int trow = 4 * g16 + (i16 >> 2);
+    const int trd = trow * ROWB + 8 * (i16 & 1);
+    const int tsw = swz16(trow);
+    const int tc = (i16 & 3) >> 1;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) roff[s] = rrd + 16 * ((4 * s + g16) ^ rsw);
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) toff[ds] = trd + 16 * ((2 * ds + tc) ^ tsw);
+  }
   const float c2 = a.scale_log2;
 
-  auto compute = [&](const unsigned char* sb, int t) __attribute__((always_inline)) {
-    const unsigned char* qb = sb;
-    const unsigned char* ob = sb + TILE;
-    const float* lse_s = reinterpret_cast<const float*>(sb + 2 * TILE);
-    const float* dl_s = lse_s + 64;
-    f32x4 sacc[2][KS], pacc[2][KS];
+  using Acc = f32x4[2][KS];
+  // S = Q K^T (role P, rows of the Q tile) or dP = dO V^T (role dS, rows of the dO tile)
+  auto products = [&](const unsigned char* rows, Acc& sacc) __attribute__((always_inline)) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int ks = 0; ks < KS; ++ks) sacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
-        const int o = qs * 16 * ROWB + rrd + 16 * ((4 * s + g16) ^ rsw);
-        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + o));
-        const bf16x8 oa = as_bf16x8(*reinterpret_cast<const u32x4*>(ob + o));
+        const int o = qs * 16 * ROWB + roff[s];
+        const bf16x8 ra = as_bf16x8(*reinterpret_cast<const u32x4*>(rows + o));
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sacc[qs][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[ks][s], sacc[qs][ks],
+        for (int ks = 0; ks < KS; ++ks)
+          sacc[qs][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, kvf[ks][s], sacc[qs][ks],
                                                                  0, 0, 0);
-          pacc[qs][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[ks][s], pacc[qs][ks],
-                                                                 0, 0, 0);
-        }
       }
-    // P and dS; queries 16 qs + 4 (l/16) + i of the tile, key l%16 of each sub-tile
+  };
+  // acc^T += X^T B over the tile whose rows are in `rows` (dO for role P, Q for role dS)
+  auto accumulate = [&](const unsigned char* rows, const bf16x8 (&bop)[KS])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int o = toff[ds];
+      const u32x2 lo = lds_read_tr16(rows + o), hi = lds_read_tr16(rows + o + 16 * ROWB);
+      const bf16x8 xt = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc[ds][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xt, bop[ks], acc[ds][ks], 0, 0, 0);
+    }
+  };
+  // k order of the B operands permuted to the accumulator layout: position 8g + e is
+  // query 4g + e (e < 4) of query sub-tile 0 and 4g + e - 4 of sub-tile 1
+  auto pack = [&](const float (&v)[2][KS][4], bf16x8 (&out)[KS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      out[ks] = as_bf16x8(u32x4{pack_bf16x2(v[0][ks][0], v[0][ks][1]),
+                                pack_bf16x2(v[0][ks][2], v[0][ks][3]),
+                                pack_bf16x2(v[1][ks][0], v[1][ks][1]),
+                                pack_bf16x2(v[1][ks][2], v[1][ks][3])});
+  };
+  // role P, tile t in stage sb: P to the exchange buffer, dV^T += dO^T P (sacc: the
+  // registers role dS keeps its dP in)
+  auto step_p = [&](const unsigned char* sb, float* xb, Acc& sacc)
+      __attribute__((always_inline)) {
+    products(sb, sacc);
+    const float* lse_s = reinterpret_cast<const float*>(sb + 2 * TILE);
+    float pv[2][KS][4];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qs * 16 + 4 * g16);
-      const float4 d4 = *reinterpret_cast<const float4*>(dl_s + qs * 16 + 4 * g16);
       const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[qs][ks][i], c2, -lv[i]));
-          sacc[qs][ks][i] = pv;
-          pacc[qs][ks][i] = pv * (pacc[qs][ks][i] - dv4[i]);
-        }
-    }
-    if (t * QT + QT > nq) {   // ragged last tile (uniform branch): no P, dS past the end
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t * QT + qs * 16 + 4 * g16 + i >= nq) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              sacc[qs][ks][i] = 0.f;
-              pacc[qs][ks][i] = 0.f;
-            }
-          }
-    }
-    bf16x8 pb[KS], sbf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      pb[ks] = as_bf16x8(u32x4{pack_bf16x2(sacc[0][ks][0], sacc[0][ks][1]),
-                               pack_bf16x2(sacc[0][ks][2], sacc[0][ks][3]),
-                               pack_bf16x2(sacc[1][ks][0], sacc[1][ks][1]),
-                               pack_bf16x2(sacc[1][ks][2], sacc[1][ks][3])});
-      sbf[ks] = as_bf16x8(u32x4{pack_bf16x2(pacc[0][ks][0], pacc[0][ks][1]),
-                                pack_bf16x2(pacc[0][ks][2], pacc[0][ks][3]),
-                                pack_bf16x2(pacc[1][ks][0], pacc[1][ks][1]),
-                                pack_bf16x2(pacc[1][ks][2], pacc[1][ks][3])});
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, one 16-d tile at a time
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      const int o = trd + 16 * ((2 * ds + tc) ^ tsw);
-      const u32x2 olo = lds_read_tr16(ob + o), ohi = lds_read_tr16(ob + o + 16 * ROWB);
-      const u32x2 qlo = lds_read_tr16(qb + o), qhi = lds_read_tr16(qb + o + 16 * ROWB);
-      const bf16x8 ot = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-      const bf16x8 qt2 = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        dvacc[ds][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ot, pb[ks], dvacc[ds][ks],
-                                                                0, 0, 0);
-        dkacc[ds][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt2, sbf[ks], dkacc[ds][ks],
-                                                                0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pv[qs][ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qs][ks][i], c2, -lv[i]));
+        *reinterpret_cast<float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4) =
+            float4{pv[qs][ks][0], pv[qs][ks][1], pv[qs][ks][2], pv[qs][ks][3]};
       }
+    }
+    bf16x8 pb[KS];
+    pack(pv, pb);
+    accumulate(sb + TILE, pb);
+  };
+  // role dS: dS of the previous tile (its stage sbp, its P in xb) from dprev, then the
+  // dP of the current tile (stage sb) into dprev, then dK^T += Q^T dS
+  auto finish_ds = [&](const unsigned char* sbp, const float* xb, const Acc& dprev,
+                       bf16x8 (&sbf)[KS]) __attribute__((always_inline)) {
+    const float* dl_s = reinterpret_cast<const float*>(sbp + 2 * TILE) + 64;
+    float sv[2][KS][4];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const float4 d4 = *reinterpret_cast<const float4*>(dl_s + qs * 16 + 4 * g16);
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float4 p4 = *reinterpret_cast<const float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4);
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[qs][ks][i] = pv[i] * (dprev[qs][ks][i] - dv4[i]);
+      }
+    }
+    pack(sv, sbf);
+  };
+
+  // The last tile of a ragged stream: wave 0, whose load filled the LSE slot, writes
+  // +inf over the positions past the end once its load has landed (before the barrier
+  // that publishes the tile): P = 0 there, and so dS = 0.
+  const int tail = nq % QT;
+  auto mask_tail = [&](unsigned char* sb, int t) __attribute__((always_inline)) {
+    if (tail != 0 && t == ntiles - 1 && wu == 0) {
+      if (lane >= tail && lane < QT)
+        reinterpret_cast<float*>(sb + 2 * TILE)[lane] = __builtin_inff();
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
     }
   };
 
-  // pipeline: tile t in stage t % 4, tiles t+1, t+2 in flight while t is computed
-  int32_t noff[LPW], nxl;
-  auto step = [&](auto STc, int t) {
-    constexpr int ST = decltype(STc)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lds<(NS - 2) * PER_TILE>();   // this wave's loads of tile t have landed
-    pipeline_barrier();
-    issue_offsets(noff, nxl, stage(std::integral_constant<int, ST + NS - 1>{}));
-    tile_offsets(t + NS, noff, nxl);
-    if (wave_busy) compute(stage(STc), t);
-  };
+  int32_t noff, nxl;
+  Acc dprev;   // role dS: dP of the previous tile (role P: its S)
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dprev[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  issue_tile(0, stage0);
-  issue_tile(1, stage1);
-  issue_tile(2, stage2);
-  tile_offsets(NS - 1, noff, nxl);
-  int t = 0;
-  for (; t + NS <= ntiles; t += NS) {
-    step(I0{}, t);
-    step(I1{}, t + 1);
-    step(I2{}, t + 2);
-    step(I3{}, t + 3);
+  // one loop per role (the branch outside the loop keeps each loop's registers its own);
+  // both loops pass the same barriers
+  auto run = [&](auto RPc) __attribute__((always_inline)) {
+    constexpr bool RP = decltype(RPc)::value;
+    auto step = [&](auto STc, int t) __attribute__((always_inline)) {
+      constexpr int ST = decltype(STc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lds<PER_TILE>();   // this wave's loads of tile t have landed
+      mask_tail(stage(STc), t);
+      pipeline_barrier();
+      issue_offsets(noff, nxl, stage(std::integral_constant<int, ST + 2>{}));
+      tile_offsets(t + 3, noff, nxl);
+      if (wave_busy) {
+        if constexpr (RP) {
+          step_p(stage(STc), &xbuf[ST & 1][kg][0], dprev);
+        } else {
+          bf16x8 sbf[KS];
+          if (t > 0) finish_ds(stage(std::integral_constant<int, ST + NS - 1>{}),
+                               &xbuf[(ST + 1) & 1][kg][0], dprev, sbf);
+          products(stage(STc) + TILE, dprev);
+          if (t > 0) accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
+        }
+      }
+    };
+    issue_tile(0, stage0);
+    issue_tile(1, stage1);
+    tile_offsets(2, noff, nxl);
+    int t = 0;
+    for (; t + NS <= ntiles; t += NS) {
+      step(I0{}, t);
+      step(I1{}, t + 1);
+      step(I2{}, t + 2);
+      step(I3{}, t + 3);
+    }
+    if (t < ntiles) step(I0{}, t);
+    if (t + 1 < ntiles) step(I1{}, t + 1);
+    if (t + 2 < ntiles) step(I2{}, t + 2);
+  };
+  if (role_p) run(std::true_type{});
+  else run(std::false_type{});
+  // role dS: the dS and dK^T of the last tile, once its P is published
+  wait_vmcnt_lds<0>();   // also: the loads past the end land before the LDS is released
+  __syncthreads();
+  if (wave_busy && !role_p && ntiles > 0) {
+    const int last = ntiles - 1;
+    bf16x8 sbf[KS];
+    const float* xb = &xbuf[last & 1][kg][0];
+    switch (last & 3) {
+      case 0: finish_ds(stage0, xb, dprev, sbf); accumulate(stage0, sbf); break;
+      case 1: finish_ds(stage1, xb, dprev, sbf); accumulate(stage1, sbf); break;
+      case 2: finish_ds(stage2, xb, dprev, sbf); accumulate(stage2, sbf); break;
+      default: finish_ds(stage3, xb, dprev, sbf); accumulate(stage3, sbf); break;
+    }
   }
-  if (t < ntiles) step(I0{}, t);
-  if (t + 1 < ntiles) step(I1{}, t + 1);
-  if (t + 2 < ntiles) step(I2{}, t + 2);
-  // the loads of the tiles past the end must land before the LDS is released
-  wait_vmcnt_lds<0>();
 
-  // dK^T, dV^T tiles: lane l holds key l%16 of sub-tile ks, d = 16 ds + 4 (l/16) + 0..3
+  // dV^T (role P) or dK^T (role dS): lane l holds key l%16 of sub-tile ks,
+  // d = 16 ds + 4 (l/16) + 0..3
+  GT* __restrict__ out = role_p ? dV : dK;
+  const float osc = role_p ? 1.0f : a.scale;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (kbase + ks * 16 + i16 < klim) {
@@ -673,11 +736,8 @@ void attn_bwd_dkdv16_bf16_kernel(AttnParams a) {
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds) {
         const int d0 = ds * 16 + 4 * g16;
-        const float sc = a.scale;
-        store4(dK + koff + d0, dkacc[ds][ks][0] * sc, dkacc[ds][ks][1] * sc,
-               dkacc[ds][ks][2] * sc, dkacc[ds][ks][3] * sc);
-        store4(dV + koff + d0, dvacc[ds][ks][0], dvacc[ds][ks][1], dvacc[ds][ks][2],
-               dvacc[ds][ks][3]);
+        store4(out + koff + d0, acc[ds][ks][0] * osc, acc[ds][ks][1] * osc,
+               acc[ds][ks][2] * osc, acc[ds][ks][3] * osc);
       }
     }
   }
@@ -1208,16 +1268,16 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
 }
 
 template <bool DENSE, typename GT>
-static void launch_dkdv16_bf16(AttnParams a, hipStream_t s) {
+static void launch_dkdv_split_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 191) / 192;
   const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dkdv16_bf16_kernel<DENSE, !DENSE, GT><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT><<<grid, 512, 0, s>>>(a);
   else
-    attn_bwd_dkdv16_bf16_kernel<DENSE, false, GT><<<grid, 256, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT><<<grid, 512, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT, bool TOK = false>
@@ -1226,9 +1286,10 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128 && !TOK) {
-    // 48 keys per wave when 192-key tiles pad a block no more than 128-key ones
+    // 192 keys a workgroup (key groups of 48) when 192-key tiles pad a block no more
+    // than 128-key ones
     if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
-      launch_dkdv16_bf16<DENSE, GT>(a, s);
+      launch_dkdv_split_bf16<DENSE, GT>(a, s);
       return;
     }
   }
