@@ -105,6 +105,7 @@ def _kernel_source_hash(kernel):
     src = {"attn_fwd_bf16_kernel": "attn_fwd.hip", "attn_fwd16_bf16_kernel": "attn_fwd.hip",
            "attn_bwd_dkdv_bf16_kernel": "attn_bwd.hip",
            "attn_bwd_dkdv_split_bf16_kernel": "attn_bwd.hip",
+           "attn_bwd_dq_split_bf16_kernel": "attn_bwd.hip",
            "attn_bwd_dq_bf16_kernel": "attn_bwd.hip"}[kernel]
     h = hashlib.sha256()
     for fn in (src, "attn_common.h", "device_common.h"):
@@ -149,6 +150,14 @@ def dkdv_kernel_name(klim, head_dim, bf16):
     if bf16 and head_dim == 128 and -(-klim // 192) * 192 <= -(-klim // 128) * 128:
         return "attn_bwd_dkdv_split_bf16_kernel"
     return "attn_bwd_dkdv_bf16_kernel"
+
+
+def dq_kernel_name(qlim, head_dim, bf16):
+    """The dQ kernel the library launches: 192 queries a workgroup in query groups of 48,
+    each split over two waves, at d = 128 under the same padding rule."""
+    if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= -(-qlim // 128) * 128:
+        return "attn_bwd_dq_split_bf16_kernel"
+    return "attn_bwd_dq_bf16_kernel"
 
 
 def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
@@ -215,7 +224,7 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
     select_bytes = 2.0 * p.groups * nb * d * 4 + 6.0 * p.groups * nb * nb * 4
     kernel_names = {"fwd": fwd_kernel_name(S, d, dtype == torch.bfloat16),
                     "dkdv": dkdv_kernel_name(S, d, dtype == torch.bfloat16),
-                    "dq": "attn_bwd_dq_bf16_kernel"}
+                    "dq": dq_kernel_name(S, d, dtype == torch.bfloat16)}
 
     dense = None
     if dense_reps > 0:

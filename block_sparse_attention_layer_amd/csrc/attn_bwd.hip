@@ -744,6 +744,330 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 }
 
 // ---------------------------------------------------------------------------------
+// dQ for d = 128 on v_mfma_f32_16x16x32_bf16, the layout of the 48-query forward: a
+// workgroup covers 192 queries (a whole 192-token block) in four query groups of 48
+// (three 16-query sub-tiles), streaming the keys of the row list in tiles of 32.  Per
+// tile and query group:
+//   S^T = K Q^T and dP^T = V dO^T as 2 key sub-tiles x 3 query sub-tiles x 4 d-steps
+//   (A = K or V rows from LDS, B = the group's Q or dO columns in registers); the
+//   accumulator gives lane l the query l % 16 of each query sub-tile and keys
+//   4 (l/16) + 0..3 of each key sub-tile;
+//   P = exp(S / sqrt(d) - lse), dS = P (dP - delta), packed with their k order permuted
+//   to the accumulator layout (as P in the forward): the B operand of dQ^T += K^T dS^T,
+//   whose A operand K^T comes from two transposing reads of the K tile.
+// The work of a query group is split over two waves on one SIMD (waves qg and qg + 4):
+//   role P (waves 0-3): S and P, written (fp32) to an LDS exchange buffer;
+//   role dQ (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
+//     been published by the step barrier, dS and dQ^T += K^T dS^T.
+// Only role dQ holds the dQ accumulator (96 registers a lane), so two waves fit a SIMD,
+// all eight waves have queries at 192-token blocks, and each K/V tile is loaded once per
+// block.  The K tile is read row-wise and transposed (swizzle swz16); the V tile only
+// row-wise (same swizzle).  Stages as in the split dK/dV kernel: tile t is read at steps
+// t and t+1, step t refills the stage of tile t-2 with tile t+2.
+template <bool DENSE, bool TAB, typename GT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
+  constexpr int D = 128, NW = 8, NT = 512, NQG = 4;
+  constexpr int M = 3;                       // query sub-tiles per group
+  constexpr int QW = 16 * M;                 // queries per group
+  constexpr int QT = NQG * QW;               // queries per workgroup
+  constexpr int KT = 32;                     // keys per tile
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = KT * ROWB;            // bytes of one K or V tile
+  constexpr int LPW = KT / (NW * 4);         // load instructions per wave per tensor
+  static_assert(LPW == 1, "one row group per wave");
+  constexpr int NS = 4;                      // pipeline stages
+  constexpr int PER_TILE = 2 * LPW;          // loads per wave per tile
+  constexpr int XF = 2 * M * 4 * 64;         // floats of P one query group passes a tile
+
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
+  __shared__ __attribute__((aligned(16))) float xbuf[2][NQG][XF];
+  __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
+  __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
+  __shared__ int32_t scratch[NW];
+  auto stage = [&](auto Ic) -> unsigned char* {
+    constexpr int I = decltype(Ic)::value % NS;
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
+  };
+
+  const Geom& g = a.g;
+  int grp, iblk, qt;
+  if constexpr (DENSE) {
+    const int bid = xcd_item(blockIdx.x, g.B * g.Hh, a.tiles);
+    if (bid < 0) return;
+    qt = bid % a.tiles;
+    iblk = 0;
+    grp = bid / a.tiles;
+  } else {
+    SparseItem it;
+    if (!sparse_item<NT>(g, a.row_ptr, a.tiles, a.ordered != 0, cols, scratch, &it)) return;
+    grp = it.grp;
+    iblk = it.blk;
+    qt = it.tile;
+  }
+
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(a.dout);
+  GT* __restrict__ dQ = static_cast<GT*>(a.dq);
+  const uint32_t tbytes = uint32_t(g.B * g.L * g.Hh * D) * 2u;   // < 2^32 (validated)
+  const BufRes rK = buffer_res(K, tbytes), rV = buffer_res(V, tbytes);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int qg = wu & (NQG - 1);
+  const bool role_p = wu < NQG;              // wave-uniform
+  const int g16 = lane >> 4, i16 = lane & 15;
+
+  int nkeys;
+  if constexpr (DENSE) {
+    nkeys = g.L;
+  } else {
+    int start, len;
+    list_range(g, a.row_ptr, grp, iblk, &start, &len);
+    const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
+                                      g.Nb, cols, scratch);
+    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
+    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: loads of an empty stream
+    if constexpr (TAB)
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+    __syncthreads();
+    nkeys = kept * g.S;
+  }
+  const int ntiles = (nkeys + KT - 1) / KT;
+
+  // this lane's query in each sub-tile; Q (role P) or dO (role dQ) fragments in registers
+  const int qlim = DENSE ? g.L : g.S;
+  const int qbase = qt * QT + qg * QW;
+  const bool wave_busy = qbase < qlim;   // otherwise: loads and barriers only
+  auto query_token = [&](int m) -> int32_t {
+    const int rq = qbase + m * 16 + i16;
+    const int rqc = rq < qlim ? rq : 0;
+    return DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
+  };
+  const uint16_t* __restrict__ QO = role_p ? Q : dO;
+  bf16x8 qof[M][D / 32];
+  float rowv[M];   // lse * log2(e) (role P) or delta (role dQ) of this lane's queries
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int32_t x = query_token(m);
+    const int32_t qoff = row_offset(g, grp, x);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      qof[m][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(QO + qoff + s * 32 + g16 * 8));
+    rowv[m] = role_p ? a.lse[size_t(grp) * g.L + x] * kLog2e
+                     : a.delta[size_t(grp) * g.L + x];
+  }
+
+  // loader: one instruction moves 4 rows; lane L fills row L/16 at chunk position L % 16
+  const int32_t hstride = g.Hh * D;
+  const int32_t gbase = row_offset(g, grp, 0);
+  const int plast = max(nkeys - 1, 0);   // positions past the end repeat the last key
+  const int lrow = w * (KT / NW) + g16;
+  const int chunk = (i16 ^ swz16(lrow)) * 8;
+  auto tile_offsets = [&](int t) -> int32_t {
+    const int p = min(t * KT + lrow, plast);
+    int32_t x = p;
+    if constexpr (!DENSE) {
+      const uint32_t pb = fd_div(uint32_t(p), g.div_S);
+      const uint32_t rr = uint32_t(p) - pb * uint32_t(g.S);
+      x = cols[pb] + (TAB ? offtab[rr] : block_offset(g, rr));
+    }
+    return gbase + x * hstride;
+  };
+  auto issue_offsets = [&](int32_t o, unsigned char* sb) {
+    const int dst = wu * (KT / NW) * ROWB;   // wave-uniform
+    load_to_lds16(rK, 2u * uint32_t(o + chunk), sb + dst);
+    load_to_lds16(rV, 2u * uint32_t(o + chunk), sb + TILE + dst);
+  };
+
+  // LDS read offsets of this lane: K/V rows of d-step s (key sub-tile 0), and the K^T
+  // reads of d-tile ds (keys 0..15; +16 rows for keys 16..31)
+  int roff[D / 32], toff[D / 16];
+  {
+    const int rsw = swz16(i16);
+    const int trow = 4 * g16 + (i16 >> 2);
+    const int tsw = swz16(trow);
+    const int tc = (i16 & 3) >> 1;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) roff[s] = i16 * ROWB + 16 * ((4 * s + g16) ^ rsw);
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+      toff[ds] = trow * ROWB + 8 * (i16 & 1) + 16 * ((2 * ds + tc) ^ tsw);
+  }
+  const float c2 = a.scale_log2;
+
+  using Acc = f32x4[2][M];
+  // S^T = K Q^T (role P, rows of the K tile) or dP^T = V dO^T (role dQ, rows of V)
+  auto products = [&](const unsigned char* rows, Acc& sacc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < M; ++m) sacc[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ra = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            rows + ks * 16 * ROWB + roff[s]));
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, qof[m][s], sacc[ks][m],
+                                                                0, 0, 0);
+      }
+  };
+  // role P, tile t in stage sb: P to the exchange buffer (keys past the end: P = 0)
+  auto step_p = [&](const unsigned char* sb, float* xb, int t, Acc& sacc)
+      __attribute__((always_inline)) {
+    products(sb, sacc);
+    const bool ragged = t * KT + KT > nkeys;   // uniform
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
+          if (ragged && t * KT + ks * 16 + 4 * g16 + i >= nkeys) pv[i] = 0.f;
+        }
+        *reinterpret_cast<float4*>(xb + ((ks * M + m) * 64 + lane) * 4) =
+            float4{pv[0], pv[1], pv[2], pv[3]};
+      }
+  };
+  // role dQ: dS^T of the previous tile (P in xb, dP in dprev), packed as B operands
+  auto finish_ds = [&](const float* xb, const Acc& dprev, bf16x8 (&sbf)[M])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float sv[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const float4 p4 = *reinterpret_cast<const float4*>(xb + ((ks * M + m) * 64 + lane) * 4);
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[ks][i] = pv[i] * (dprev[ks][m][i] - rowv[m]);
+      }
+      sbf[m] = as_bf16x8(u32x4{pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]),
+                               pack_bf16x2(sv[1][0], sv[1][1]), pack_bf16x2(sv[1][2], sv[1][3])});
+    }
+  };
+
+  int32_t noff;
+  Acc dprev;   // role dQ: dP^T of the previous tile (role P: its S^T)
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int m = 0; m < M; ++m) dprev[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // one loop per role (the branch outside the loop keeps each loop's registers its own);
+  // both loops pass the same barriers
+  auto run = [&](auto RPc) __attribute__((always_inline)) {
+    constexpr bool RP = decltype(RPc)::value;
+    f32x4 qacc[RP ? 1 : M][RP ? 1 : D / 16];   // role dQ: dQ^T
+    if constexpr (!RP) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) qacc[m][ds] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // dQ^T += K^T dS^T over the K tile in stage sb
+    auto accumulate = [&](const unsigned char* sb, const bf16x8 (&sbf)[M])
+        __attribute__((always_inline)) {
+      if constexpr (!RP) {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds) {
+          const u32x2 lo = lds_read_tr16(sb + toff[ds]);
+          const u32x2 hi = lds_read_tr16(sb + toff[ds] + 16 * ROWB);
+          const bf16x8 kt = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            qacc[m][ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, sbf[m], qacc[m][ds],
+                                                                  0, 0, 0);
+        }
+      }
+    };
+    auto step = [&](auto STc, int t) __attribute__((always_inline)) {
+      constexpr int ST = decltype(STc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lds<PER_TILE>();   // this wave's loads of tile t have landed
+      pipeline_barrier();
+      issue_offsets(noff, stage(std::integral_constant<int, ST + 2>{}));
+      noff = tile_offsets(t + 3);
+      if (wave_busy) {
+        if constexpr (RP) {
+          step_p(stage(STc), &xbuf[ST & 1][qg][0], t, dprev);
+        } else {
+          // the previous tile first: its dP registers are free before this tile's dP
+          if (t > 0) {
+            bf16x8 sbf[M];
+            finish_ds(&xbuf[(ST + 1) & 1][qg][0], dprev, sbf);
+            accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
+          }
+          products(stage(STc) + TILE, dprev);
+        }
+      }
+    };
+    issue_offsets(tile_offsets(0), stage0);
+    issue_offsets(tile_offsets(1), stage1);
+    noff = tile_offsets(2);
+    int t = 0;
+    for (; t + NS <= ntiles; t += NS) {
+      step(I0{}, t);
+      step(I1{}, t + 1);
+      step(I2{}, t + 2);
+      step(I3{}, t + 3);
+    }
+    if (t < ntiles) step(I0{}, t);
+    if (t + 1 < ntiles) step(I1{}, t + 1);
+    if (t + 2 < ntiles) step(I2{}, t + 2);
+    // role dQ: the dS and dQ^T of the last tile, once its P is published
+    wait_vmcnt_lds<0>();   // also: the loads past the end land before the LDS is released
+    __syncthreads();
+    if constexpr (!RP) {
+      if (wave_busy && ntiles > 0) {
+        const int last = ntiles - 1;
+        bf16x8 sbf[M];
+        finish_ds(&xbuf[last & 1][qg][0], dprev, sbf);
+        switch (last & 3) {
+          case 0: accumulate(stage0, sbf); break;
+          case 1: accumulate(stage1, sbf); break;
+          case 2: accumulate(stage2, sbf); break;
+          default: accumulate(stage3, sbf); break;
+        }
+      }
+      // dQ^T: lane l holds query l%16 of sub-tile m, d = 16 ds + 4 (l/16) + 0..3
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (qbase + m * 16 + i16 < qlim) {
+          const int32_t qoff = row_offset(g, grp, query_token(m));
+#pragma unroll
+          for (int ds = 0; ds < D / 16; ++ds) {
+            const int d0 = ds * 16 + 4 * g16;
+            const float sc = a.scale;
+            store4(dQ + qoff + d0, qacc[m][ds][0] * sc, qacc[m][ds][1] * sc,
+                   qacc[m][ds][2] * sc, qacc[m][ds][3] * sc);
+          }
+        }
+      }
+    }
+  };
+  if (role_p) run(std::true_type{});
+  else run(std::false_type{});
+}
+
+// ---------------------------------------------------------------------------------
 // dQ: one wave per 32 queries, key stream from the row list of the query block.
 // TOK: token-granular selection, as in the forward (list-position mask of the query).
 // NS: K/V tile stages.  With 4, step t waits only for this wave's loads of tile t, passes
@@ -1302,11 +1626,32 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
     attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, false, GT, TOK><<<grid, NWK * 64, 0, s>>>(a);
 }
 
+template <bool DENSE, typename GT>
+static void launch_dq_split_bf16(AttnParams a, hipStream_t s) {
+  const Geom& g = a.g;
+  const int lim = DENSE ? g.L : g.S;
+  const int rows = DENSE ? 1 : g.Nb;
+  a.tiles = (lim + 191) / 192;
+  const int grid = launch_grid<DENSE>(a, rows);
+  if (!DENSE && g.S <= kOffsetTable)
+    attn_bwd_dq_split_bf16_kernel<DENSE, !DENSE, GT><<<grid, 512, 0, s>>>(a);
+  else
+    attn_bwd_dq_split_bf16_kernel<DENSE, false, GT><<<grid, 512, 0, s>>>(a);
+}
+
 template <int D, bool DENSE, typename GT, bool TOK = false>
 static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int KSUB = D == 128 ? 1 : 2;   // staging needs KSUB*32*D/8 to split over 4 waves
   const int lim = DENSE ? g.L : g.S;
+  if constexpr (D == 128 && !TOK) {
+    // 192 queries a workgroup (query groups of 48) when 192-query tiles pad a block no
+    // more than 128-query ones
+    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
+      launch_dq_split_bf16<DENSE, GT>(a, s);
+      return;
+    }
+  }
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 127) / 128;
   const int grid = launch_grid<DENSE>(a, rows);
