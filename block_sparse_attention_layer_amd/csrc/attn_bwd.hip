@@ -1646,8 +1646,12 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128 && !TOK) {
     // 192 queries a workgroup (query groups of 48) when 192-query tiles pad a block no
-    // more than 128-query ones
-    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
+    // more than 128-query ones and 128-query tiles would leave more than an eighth of
+    // their query slots empty (192-token blocks: a quarter).  Its two roles are not
+    // balanced (role P has half the products of role dQ), which costs more than the
+    // empty slots save on long blocks.
+    const int p128 = (lim + 127) / 128 * 128;
+    if ((lim + 191) / 192 * 192 <= p128 && (p128 - lim) * 8 > p128) {
       launch_dq_split_bf16<DENSE, GT>(a, s);
       return;
     }
