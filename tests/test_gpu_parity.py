@@ -33,6 +33,9 @@ CASES = [
     ("small1d_120", "l1d_32k", dict(T=6, H=10, W=12), LayerSpec(0, (1, 10, 12)), 0.25, "bf16", 128, 1),
     ("small3d_d64_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.5, "bf16", 64, 2),
     ("small3d_fp32", "l3d_55k", dict(T=4, H=12, W=16), LayerSpec(2, (2, 6, 8)), 0.3, "fp32", 128, 1),
+    # d = 128, 192-token blocks, two batch entries: the split dK/dV and dQ kernels over
+    # head groups of both
+    ("small3d_192_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.8, "bf16", 128, 2),
     # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and dK/dV
     # kernels, three 128-query tiles in dQ, and a block count that is no multiple of 8
     ("tiles2_3d_384", "l3d_55k", dict(T=8, H=36, W=16), LayerSpec(2, (4, 12, 8)), 0.6, "bf16", 128, 1),
