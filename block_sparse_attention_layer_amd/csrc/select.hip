@@ -587,8 +587,8 @@ __global__ __launch_bounds__(kSelThreads) void emit_lists_kernel(
 //   pool_hist_kernel   one per 8-bit digit: (count, fixed-point mass) histograms of the keys
 //                      that match the digits decided so far, merged with global atomics
 //                      (integer sums, so the order of the atomics does not matter);
-//   pool_step_kernel   one thread per head group walks the merged histogram down from the
-//                      top digit to where the running mass (or count) reaches the target;
+//   pool_step_kernel   one wave per head group finds where the walk down the merged
+//                      histogram from the top digit reaches the target mass (or count);
 //   pool_ties_*        only when the cut falls inside a run of equal keys: the ranks of the
 //                      tied pairs in linear order (per-chunk counts, then a scan);
 //   pool_emit_kernel   the row bitmap [G][rows][W] (W = ceil(N_b/32) words per row) and,
@@ -729,29 +729,53 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(int rows, int Nb, int rp
 // After digit pass `pass`: pick the digit where the running mass (topk > 0: count)
 // reaches the target.  One wave per head group: the lanes copy the merged histogram to
 // LDS and clear it for the next pass, then lane 0 walks the copy.
+// Inclusive prefix sum over the 64 lanes of a wave (lane 0 first), of a 64-bit value.
+__device__ __forceinline__ unsigned long long wave_prefix_u64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = __shfl_up(uint32_t(v), off, 64);
+    const uint32_t hi = __shfl_up(uint32_t(v >> 32), off, 64);
+    if (lane >= off) v += (static_cast<unsigned long long>(hi) << 32) | lo;
+  }
+  return v;
+}
+
+// The walk down the merged histogram, one wave per head group: lane L holds digits
+// 255 - 4L ... 252 - 4L.  A prefix sum over the lanes gives every lane the mass and count
+// of the digits above its four; each lane then tests its digits in descending order for
+// the stop rule (a non-empty digit at which the running mass, or count, reaches the
+// target), and the lowest lane with a hit holds the digit the sequential walk from the
+// top digit stops at.
 __global__ __launch_bounds__(64) void pool_step_kernel(int pass, float tau, int topk,
                                                        double npairs,
                                                        PoolState* __restrict__ st,
                                                        uint32_t* __restrict__ hcnt,
                                                        unsigned long long* __restrict__ hmass) {
-  __shared__ uint32_t c[256];
-  __shared__ unsigned long long ms[256];
   const int grp = blockIdx.x, lane = threadIdx.x;
   uint32_t* gc = hcnt + grp * 256;
   unsigned long long* gm = hmass + grp * 256;
-  for (int d = lane; d < 256; d += 64) {
-    c[d] = gc[d];
-    ms[d] = gm[d];
+  uint32_t c4[4];
+  unsigned long long m4[4];
+  uint32_t csum = 0;
+  unsigned long long msum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = 255 - 4 * lane - j;
+    c4[j] = gc[d];
+    m4[j] = gm[d];
     gc[d] = 0u;
     gm[d] = 0ull;
+    csum += c4[j];
+    msum += m4[j];
   }
-  __syncthreads();
-  if (lane != 0) return;
-  PoolState& S = st[grp];
+  PoolState S = st[grp];
   const bool count = topk > 0;
+  const unsigned long long mincl = wave_prefix_u64(msum, lane);
+  const unsigned long long cincl = wave_prefix_u64(csum, lane);
   if (pass == 0) {   // every pair matched: the histogram holds the whole pool
-    unsigned long long z = 0;
-    for (int d = 0; d < 256; ++d) z += ms[d];
+    const unsigned long long z = __shfl(uint32_t(mincl), 63, 64) |
+                                 (static_cast<unsigned long long>(
+                                      __shfl(uint32_t(mincl >> 32), 63, 64)) << 32);
     S.Z = z;
     if (count) {
       S.R = (unsigned long long)topk;
@@ -764,26 +788,38 @@ __global__ __launch_bounds__(64) void pool_step_kernel(int pass, float tau, int 
     S.above_cnt = 0;
     S.prefix = 0;
   }
-  if (S.select_all) return;
-  const int shift = 24 - 8 * pass;
-  unsigned long long acc = S.above_mass;
-  uint32_t n = S.above_cnt;
-  int dg = 255;
-  for (; dg >= 0; --dg) {
-    const bool reach = count ? n + c[dg] >= S.R : acc + ms[dg] >= S.R;
-    if (c[dg] > 0 && reach) break;
-    acc += ms[dg];
-    n += c[dg];
-  }
-  if (dg < 0) {
-    S.select_all = 1u;   // rounding kept the total below the target
+  if (S.select_all) {   // uniform
+    if (lane == 0 && pass == 0) st[grp] = S;
     return;
   }
+  // this lane's digits in descending order, from the totals above them
+  unsigned long long acc = S.above_mass + (mincl - msum);
+  uint32_t n = S.above_cnt + uint32_t(cincl - csum);
+  int hit = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool reach = count ? n + c4[j] >= S.R : acc + m4[j] >= S.R;
+    if (hit < 0 && c4[j] > 0 && reach) hit = j;
+    if (hit < 0) {
+      acc += m4[j];
+      n += c4[j];
+    }
+  }
+  const uint64_t hits = __ballot(hit >= 0);
+  if (hits == 0) {   // rounding kept the total below the target
+    if (lane == 0) {
+      S.select_all = 1u;
+      st[grp] = S;
+    }
+    return;
+  }
+  if (lane != __builtin_ctzll(hits)) return;
+  const int dg = 255 - 4 * lane - hit;
   S.above_mass = acc;
   S.above_cnt = n;
-  S.prefix |= uint32_t(dg) << shift;
-  S.tie_cnt = c[dg];
-  S.tie_mass = ms[dg];
+  S.prefix |= uint32_t(dg) << (24 - 8 * pass);
+  S.tie_cnt = c4[hit];
+  S.tie_mass = m4[hit];
   if (pass == 3) {
     // all tied pairs share one score, hence one fixed-point mass
     const unsigned long long e1 = S.tie_mass / S.tie_cnt;
@@ -794,6 +830,7 @@ __global__ __launch_bounds__(64) void pool_step_kernel(int pass, float tau, int 
     S.take = uint32_t(t);
     S.need_rank = S.take < S.tie_cnt ? 1u : 0u;
   }
+  st[grp] = S;
 }
 
 // Tied pairs (key equal to the cut) per chunk, when only some of them are taken.
