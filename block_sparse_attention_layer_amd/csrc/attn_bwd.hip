@@ -396,7 +396,10 @@ __device__ __forceinline__ int swz16(int r) { return 2 * (r & 7); }
 // the loads of a tile have two steps to land).  The exchange buffer alternates with the
 // tile's parity: role P writes tile t's half at step t, role dS reads it at step t+1,
 // and role P overwrites it at step t+2, after the barrier that ends step t+1.
-template <bool DENSE, bool TAB, typename GT>
+// TOK: token-granular selection; role P keeps P only where the query token's key-block
+// mask has this block's bit (dS then vanishes with it).  Wave 2 loads the tile's mask
+// words into its slot instead of an LSE copy.
+template <bool DENSE, bool TAB, typename GT, bool TOK = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 8, NT = 512, NKG = 4;
@@ -511,6 +514,9 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   const float* dl_g = a.delta + size_t(grp) * g.L;
   const BufRes rL = buffer_res(lse_g, uint32_t(g.L) * 4u);
   const BufRes rD = buffer_res(dl_g, uint32_t(g.L) * 4u);
+  // key-block mask words: G * L * mwords * 4 < 2^32 bytes (validated)
+  const BufRes rM = buffer_res(a.tokmask, TOK ? uint32_t(g.B * g.Hh * g.L * a.mwords) * 4u : 0u);
+  const uint32_t mword = TOK ? uint32_t(grp * g.L) * uint32_t(a.mwords) + uint32_t(jblk >> 5) : 0u;
   const int32_t hstride = g.Hh * D;
   const int32_t gbase = row_offset(g, grp, 0);
   const int plast = max(nq - 1, 0);   // positions past the end repeat the last query
@@ -535,7 +541,10 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
     load_to_lds16(rQ, 2u * uint32_t(o + chunk), sb + dst);
     load_to_lds16(rO, 2u * uint32_t(o + chunk), sb + TILE + dst);
     // scalar branch: the descriptor stays uniform
-    if (wu & 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
+    if (TOK && wu == 2)
+      load_to_lds4(rM, 4u * (mword + uint32_t(xl) * uint32_t(a.mwords)),
+                   sb + 2 * TILE + wu * 64 * 4);
+    else if (wu & 1) load_to_lds4(rD, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
     else load_to_lds4(rL, 4u * uint32_t(xl), sb + 2 * TILE + wu * 64 * 4);
   };
   auto issue_tile = [&](int t, unsigned char* sb) {
@@ -614,11 +623,21 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
     for (int qs = 0; qs < 2; ++qs) {
       const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qs * 16 + 4 * g16);
       const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      bool keep[4] = {true, true, true, true};
+      if constexpr (TOK) {   // select, not multiply: an empty row has lse = -inf
+        const u32x4 m4 = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint32_t*>(sb + 2 * TILE + 2 * 64 * 4) + qs * 16 + 4 * g16);
+        const uint32_t jb = uint32_t(jblk) & 31u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) keep[i] = (m4[i] >> jb) & 1u;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
           pv[qs][ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qs][ks][i], c2, -lv[i]));
+          if constexpr (TOK) pv[qs][ks][i] = keep[i] ? pv[qs][ks][i] : 0.f;
+        }
         *reinterpret_cast<float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4) =
             float4{pv[qs][ks][0], pv[qs][ks][1], pv[qs][ks][2], pv[qs][ks][3]};
       }
@@ -1591,7 +1610,7 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
                                          static_cast<const T*>(dout), delta);
 }
 
-template <bool DENSE, typename GT>
+template <bool DENSE, typename GT, bool TOK = false>
 static void launch_dkdv_split_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   const int lim = DENSE ? g.L : g.S;
@@ -1599,9 +1618,9 @@ static void launch_dkdv_split_bf16(AttnParams a, hipStream_t s) {
   a.tiles = (lim + 191) / 192;
   const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK><<<grid, 512, 0, s>>>(a);
   else
-    attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT, TOK><<<grid, 512, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT, bool TOK = false>
@@ -1609,11 +1628,11 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
-  if constexpr (D == 128 && !TOK) {
+  if constexpr (D == 128) {
     // 192 keys a workgroup (key groups of 48) when 192-key tiles pad a block no more
     // than 128-key ones
     if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
-      launch_dkdv_split_bf16<DENSE, GT>(a, s);
+      launch_dkdv_split_bf16<DENSE, GT, TOK>(a, s);
       return;
     }
   }
