@@ -783,7 +783,10 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 // block.  The K tile is read row-wise and transposed (swizzle swz16); the V tile only
 // row-wise (same swizzle).  Stages as in the split dK/dV kernel: tile t is read at steps
 // t and t+1, step t refills the stage of tile t-2 with tile t+2.
-template <bool DENSE, bool TAB, typename GT>
+// TOK: token-granular selection; role P keeps P only at the list positions its query
+// selected (the query's row of the list-position mask, two words cached per sub-tile and
+// refetched when a tile moves into another 32-position window).
+template <bool DENSE, bool TAB, typename GT, bool TOK = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 8, NT = 512, NQG = 4;
@@ -943,11 +946,29 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
                                                                 0, 0, 0);
       }
   };
-  // role P, tile t in stage sb: P to the exchange buffer (keys past the end: P = 0)
+  PosMask pm[TOK ? M : 1];
+  if constexpr (TOK) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      pm[m].init(a.posmask + size_t(grp * g.L + query_token(m)) * a.mwords, a.mwords);
+  }
+  // role P, tile t in stage sb: P to the exchange buffer (keys past the end, and with TOK
+  // unselected list positions: P = 0, by a select since an empty row has lse = -inf)
   auto step_p = [&](const unsigned char* sb, float* xb, int t, Acc& sacc)
       __attribute__((always_inline)) {
     products(sb, sacc);
     const bool ragged = t * KT + KT > nkeys;   // uniform
+    int li[2][4];   // list position of each of this lane's keys (TOK)
+    if constexpr (TOK) {
+      const int li0 = int(fd_div(uint32_t(t * KT), g.div_S));
+#pragma unroll
+      for (int m = 0; m < M; ++m) pm[m].fetch(li0);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          li[ks][i] = int(fd_div(uint32_t(t * KT + ks * 16 + 4 * g16 + i), g.div_S));
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -957,6 +978,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
         for (int i = 0; i < 4; ++i) {
           pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
           if (ragged && t * KT + ks * 16 + 4 * g16 + i >= nkeys) pv[i] = 0.f;
+          if constexpr (TOK) pv[i] = pm[m].keep(li[ks][i]) ? pv[i] : 0.f;
         }
         *reinterpret_cast<float4*>(xb + ((ks * M + m) * 64 + lane) * 4) =
             float4{pv[0], pv[1], pv[2], pv[3]};
@@ -1645,7 +1667,7 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
     attn_bwd_dkdv_bf16_kernel<D, NWK, DENSE, false, GT, TOK><<<grid, NWK * 64, 0, s>>>(a);
 }
 
-template <bool DENSE, typename GT>
+template <bool DENSE, typename GT, bool TOK = false>
 static void launch_dq_split_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   const int lim = DENSE ? g.L : g.S;
@@ -1653,9 +1675,9 @@ static void launch_dq_split_bf16(AttnParams a, hipStream_t s) {
   a.tiles = (lim + 191) / 192;
   const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dq_split_bf16_kernel<DENSE, !DENSE, GT><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dq_split_bf16_kernel<DENSE, !DENSE, GT, TOK><<<grid, 512, 0, s>>>(a);
   else
-    attn_bwd_dq_split_bf16_kernel<DENSE, false, GT><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dq_split_bf16_kernel<DENSE, false, GT, TOK><<<grid, 512, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT, bool TOK = false>
@@ -1663,7 +1685,7 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   constexpr int KSUB = D == 128 ? 1 : 2;   // staging needs KSUB*32*D/8 to split over 4 waves
   const int lim = DENSE ? g.L : g.S;
-  if constexpr (D == 128 && !TOK) {
+  if constexpr (D == 128) {
     // 192 queries a workgroup (query groups of 48) when 192-query tiles pad a block no
     // more than 128-query ones and 128-query tiles would leave more than an eighth of
     // their query slots empty (192-token blocks: a quarter).  Its two roles are not
@@ -1671,7 +1693,7 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
     // empty slots save on long blocks.
     const int p128 = (lim + 127) / 128 * 128;
     if ((lim + 191) / 192 * 192 <= p128 && (p128 - lim) * 8 > p128) {
-      launch_dq_split_bf16<DENSE, GT>(a, s);
+      launch_dq_split_bf16<DENSE, GT, TOK>(a, s);
       return;
     }
   }
