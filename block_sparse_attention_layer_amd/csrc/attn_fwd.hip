@@ -227,23 +227,25 @@ void attn_fwd_bf16_kernel(AttnParams a) {
         }
     }
   };
-  // max over the tile's keys of this lane's query: the lane's own 16*KSUB scores, then the
-  // other lane half (lane l ^ 32 holds the other keys of the same query)
+  // max over this lane's own 16*KSUB scores of the tile (lane l ^ 32 holds the other keys
+  // of the same query)
   auto tile_max = [&](const f32x16 (&acc)[KSUB]) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) mx = max3f(mx, acc[kt][v], acc[kt][v + 1]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                      false, false);
-    return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    return mx;
   };
   // lazy rescale: keep the running max unless the tile's max exceeds it by the margin
-  // (every lane on the first tile, rarely afterwards)
+  // (every lane on the first tile, rarely afterwards).  The query's max exceeds the margin
+  // exactly when one of its two lanes' maxima does; the two are combined only here.
   auto maybe_rescale = [&](float mx) {
-    const bool grow = mx > m_run + thr;
-    if (__ballot(grow)) {
+    if (__ballot(mx > m_run + thr)) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const bool grow = mx > m_run + thr;
       const float m_new = grow ? mx : m_run;
       // (with token masks a lane that has seen only masked keys keeps m = -inf, and
       // -inf - -inf would make its alpha NaN)
@@ -260,7 +262,8 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   auto softmax_pack = [&](const f32x16 (&acc)[KSUB], u32x4 (&pw)[2 * KSUB]) {
     // (with token masks a query may have seen only masked keys so far: m = -inf, P = 0)
     const float moff = (TOK && m_run == -INFINITY) ? 0.f : m_run * c2;
-    float psum = 0.f;
+    // the row sum takes the same bf16 P as the product with V, two at a time
+    float psum = l_run;
 #pragma unroll
     for (int ks = 0; ks < 2 * KSUB; ++ks) {
       const int kt = ks >> 1, g0 = (ks & 1) * 8;
@@ -268,11 +271,11 @@ void attn_fwd_bf16_kernel(AttnParams a) {
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[kt][g0 + 2 * e], c2, -moff));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[kt][g0 + 2 * e + 1], c2, -moff));
-        psum += p0 + p1;
         pw[ks][e] = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(pw[ks][e], psum);
       }
     }
-    l_run += psum;
+    l_run = psum;
   };
   // O^T += V^T P^T, 16 keys per step; V^T fragments by transposing reads
   auto pv_update = [&](const unsigned char* smem, const u32x4 (&pw)[2 * KSUB]) {
@@ -579,7 +582,18 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
             for (int m = 0; m < M; ++m) sacc[ks][m][i] = -INFINITY;
           }
     }
-    // per query: max over the lane's 8 scores, then over the four 16-lane groups
+    // per query: max over the lane's 8 scores, then over the four 16-lane groups.  A row's
+    // max exceeds m_run + thr exactly when one of its four lanes' maxima does, so the sparse
+    // kernels test the lanes' own maxima and exchange them only to rescale (the dense one
+    // exchanges them first: deferred, its registers spill inside the loop)
+    auto row_max = [&](float v) __attribute__((always_inline)) {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+      v = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                        false, false);
+      return __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    };
     float mx[M];
     bool any = false;
 #pragma unroll
@@ -588,19 +602,15 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
       v = max3f(v, sacc[0][m][3], sacc[1][m][0]);
       v = max3f(v, sacc[1][m][1], sacc[1][m][2]);
       v = __builtin_elementwise_maximum(v, sacc[1][m][3]);
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                        false, false);
-      v = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                        false, false);
-      mx[m] = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      mx[m] = DENSE ? row_max(v) : v;
       any |= mx[m] > m_run[m] + thr;
     }
     // lazy rescale (wave-uniform): every sub-tile on the first tile, rarely afterwards
     if (__ballot(any)) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float m_new = mx[m] > m_run[m] + thr ? mx[m] : m_run[m];
+        const float v = DENSE ? mx[m] : row_max(mx[m]);
+        const float m_new = v > m_run[m] + thr ? v : m_run[m];
         const float alpha = __builtin_amdgcn_exp2f((m_run[m] - m_new) * c2);
         l_run[m] *= alpha;
 #pragma unroll
@@ -619,10 +629,19 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           p[ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -moff));
-      l_run[m] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                  ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
       pw[m] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                     pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+      // the sparse kernels' row sum takes the same bf16 P as the product with V, two at a
+      // time (the dense one sums the fp32 P: with the dot products its registers spill)
+      if constexpr (DENSE) {
+        l_run[m] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                    ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      } else {
+        float l = l_run[m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l = sum_bf16x2(pw[m][j], l);
+        l_run[m] = l;
+      }
     }
     // O^T += V^T P^T
 #pragma unroll
