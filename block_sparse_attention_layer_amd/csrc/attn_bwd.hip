@@ -958,16 +958,20 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
       __attribute__((always_inline)) {
     products(sb, sacc);
     const bool ragged = t * KT + KT > nkeys;   // uniform
-    int li[2][4];   // list position of each of this lane's keys (TOK)
+    // TOK: the launcher takes this kernel only for blocks of more than 128 tokens, so the
+    // tile's keys lie at list positions li0 (offsets below the boundary) and li0 + 1: two
+    // mask bits a query, and one compare a key
+    bool b0[TOK ? M : 1], b1[TOK ? M : 1];
+    int bh = 0;   // the boundary, counted from this lane's first key
     if constexpr (TOK) {
       const int li0 = int(fd_div(uint32_t(t * KT), g.div_S));
 #pragma unroll
-      for (int m = 0; m < M; ++m) pm[m].fetch(li0);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          li[ks][i] = int(fd_div(uint32_t(t * KT + ks * 16 + 4 * g16 + i), g.div_S));
+      for (int m = 0; m < M; ++m) {
+        pm[m].fetch(li0);
+        b0[m] = pm[m].keep(li0);
+        b1[m] = pm[m].keep(li0 + 1);
+      }
+      bh = (li0 + 1) * g.S - t * KT - 4 * g16;
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -978,7 +982,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
         for (int i = 0; i < 4; ++i) {
           pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
           if (ragged && t * KT + ks * 16 + 4 * g16 + i >= nkeys) pv[i] = 0.f;
-          if constexpr (TOK) pv[i] = pm[m].keep(li[ks][i]) ? pv[i] : 0.f;
+          if constexpr (TOK) pv[i] = ((ks * 16 + i) < bh ? b0[m] : b1[m]) ? pv[i] : 0.f;
         }
         *reinterpret_cast<float4*>(xb + ((ks * M + m) * 64 + lane) * 4) =
             float4{pv[0], pv[1], pv[2], pv[3]};
@@ -1270,18 +1274,33 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
       const uint32_t p0 = uint32_t(t * KT);
       const int wi = int(fd_div(p0, g.div_S)) >> 5;
       const uint32_t w0 = pw0, w1 = pw1;
-      // opaque per-tile base: otherwise the 16 per-key lane offsets are hoisted out of the
-      // loop into 16 registers
-      uint32_t pb = p0 + 4 * half;
-      asm volatile("" : "+v"(pb));
+      if (g.S >= KT) {
+        // the tile spans list positions li0 (offsets below the boundary) and li0 + 1: two
+        // mask bits, and one compare a key
+        const int li0 = int(fd_div(p0, g.div_S));
+        const int r0 = li0 - 32 * wi, r1 = r0 + 1;
+        const uint32_t b0 = (w0 >> r0) & 1u;
+        const uint32_t b1 = (((r1 < 32) ? w0 : w1) >> (r1 & 31)) & 1u;
+        const int bh = (li0 + 1) * g.S - int(p0) - 4 * half;   // from this lane's first key
 #pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk)
+        for (int kk = 0; kk < KSUB; ++kk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t p = pb + (kk * 32 + 8 * (v >> 2) + (v & 3));
-          const int rel = int(fd_div(p, g.div_S)) - 32 * wi;
-          keepbits |= ((((rel < 32) ? w0 : w1) >> (rel & 31)) & 1u) << (kk * 16 + v);
-        }
+          for (int v = 0; v < 16; ++v)
+            keepbits |= ((kk * 32 + 8 * (v >> 2) + (v & 3)) < bh ? b0 : b1) << (kk * 16 + v);
+      } else {
+        // opaque per-tile base: otherwise the 16 per-key lane offsets are hoisted out of
+        // the loop into 16 registers
+        uint32_t pb = p0 + 4 * half;
+        asm volatile("" : "+v"(pb));
+#pragma unroll
+        for (int kk = 0; kk < KSUB; ++kk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t p = pb + (kk * 32 + 8 * (v >> 2) + (v & 3));
+            const int rel = int(fd_div(p, g.div_S)) - 32 * wi;
+            keepbits |= ((((rel < 32) ? w0 : w1) >> (rel & 31)) & 1u) << (kk * 16 + v);
+          }
+      }
       // keep the computation here: sunk to its use it lands where registers are scarcest
       asm volatile("" : "+v"(keepbits));
     }
@@ -1693,6 +1712,7 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
     // empty slots save on long blocks.
     const int p128 = (lim + 127) / 128 * 128;
     if ((lim + 191) / 192 * 192 <= p128 && (p128 - lim) * 8 > p128) {
+      // (this implies lim > 128, as the token instance's two-position key tiles need)
       launch_dq_split_bf16<DENSE, GT, TOK>(a, s);
       return;
     }

@@ -215,16 +215,31 @@ void attn_fwd_bf16_kernel(AttnParams a) {
   auto mask_tokens = [&](f32x16 (&acc)[KSUB], int t) {
     if constexpr (TOK) {
       const uint32_t p0 = uint32_t(t * KT);
-      pm.fetch(int(fd_div(p0, g.div_S)));
-      uint32_t pb = p0 + 4 * half;   // opaque, so the per-key offsets are not hoisted
-      asm volatile("" : "+v"(pb));
+      const int li0 = int(fd_div(p0, g.div_S));
+      pm.fetch(li0);
+      if (g.S >= KT) {
+        // the tile spans list positions li0 (offsets below bnd) and li0 + 1 only: two
+        // mask bits a tile, and one compare a key against the boundary
+        const bool b0 = pm.keep(li0), b1 = pm.keep(li0 + 1);
+        const int bh = (li0 + 1) * g.S - t * KT - 4 * half;   // from this lane's first key
 #pragma unroll
-      for (int kt = 0; kt < KSUB; ++kt)
+        for (int kt = 0; kt < KSUB; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const uint32_t p = pb + (kt * 32 + 8 * (v >> 2) + (v & 3));
-          if (!pm.keep(int(fd_div(p, g.div_S)))) acc[kt][v] = -INFINITY;
-        }
+          for (int v = 0; v < 16; ++v) {
+            const bool kp = (kt * 32 + 8 * (v >> 2) + (v & 3)) < bh ? b0 : b1;
+            if (!kp) acc[kt][v] = -INFINITY;
+          }
+      } else {
+        uint32_t pb = p0 + 4 * half;   // opaque, so the per-key offsets are not hoisted
+        asm volatile("" : "+v"(pb));
+#pragma unroll
+        for (int kt = 0; kt < KSUB; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint32_t p = pb + (kt * 32 + 8 * (v >> 2) + (v & 3));
+            if (!pm.keep(int(fd_div(p, g.div_S)))) acc[kt][v] = -INFINITY;
+          }
+      }
     }
   };
   // max over this lane's own 16*KSUB scores of the tile (lane l ^ 32 holds the other keys
