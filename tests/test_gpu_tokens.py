@@ -39,6 +39,13 @@ CASES = [
     ("batch2_3d", "l3d_55k", dict(T=4, H=12, W=16, batch=2), LayerSpec(2, (4, 6, 8)), 128, 2),
     # the block-count limit: 1024 blocks of 8 tokens, 32 mask words per token
     ("max_blocks_3d", "l3d_55k", dict(T=8, H=32, W=32), LayerSpec(2, (2, 2, 2)), 64, 1),
+    # block sizes around one key tile (32 keys at d = 128, 64 at d = 64): from one tile up,
+    # a tile's keys lie at two list positions at most and the kernels take two mask bits
+    # a tile; below, one bit a key
+    ("tile_exact_32", "l3d_55k", dict(T=4, H=8, W=8), LayerSpec(2, (2, 4, 4)), 128, 2),
+    ("straddle_40", "l3d_55k", dict(T=2, H=10, W=16), LayerSpec(2, (1, 5, 8)), 128, 2),
+    ("tile_exact_64_d64", "l3d_55k", dict(T=4, H=8, W=16), LayerSpec(2, (2, 4, 8)), 64, 2),
+    ("under_tile_48_d64", "l3d_55k", dict(T=4, H=8, W=12), LayerSpec(2, (2, 4, 6)), 64, 2),
 ]
 IDS = [c[0] for c in CASES]
 
