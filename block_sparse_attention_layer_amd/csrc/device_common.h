@@ -58,10 +58,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// x from the lane that DPP control CTRL names (a permutation inside each row of 16).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(x)), CTRL, 0xf, 0xf, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(x >> 32)), CTRL, 0xf, 0xf, false));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Sum over the 64 lanes of a wave, returned to every lane, without going through LDS:
+// DPP swaps inside quads (lane ^ 1, ^ 2), then mirrors inside half rows and rows of 16,
+// then the swaps of rows 0/1 with 2/3... (lane ^ 16) and of the two halves (lane ^ 32).
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_u64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_u64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_u64<0x141>(v);   // row_half_mirror
+  v += dpp_u64<0x140>(v);   // row_mirror
+  const uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  v = ((uint64_t(h16[0]) << 32) | l16[0]) + ((uint64_t(h16[1]) << 32) | l16[1]);
+  const uint32_t lo2 = uint32_t(v), hi2 = uint32_t(v >> 32);
+  const auto l32 = __builtin_amdgcn_permlane32_swap(lo2, lo2, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(hi2, hi2, false, false);
+  return ((uint64_t(h32[0]) << 32) | l32[0]) + ((uint64_t(h32[1]) << 32) | l32[1]);
 }
 
 inline int launch_status() {

@@ -710,14 +710,24 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(int rows, int Nb, int rp
   const size_t begin = size_t(blockIdx.x) * rpc * Nb;
   const size_t end = min(N, begin + size_t(rpc) * Nb);
   const float* s = scores + size_t(grp) * N;
-  for (size_t base = begin; base < end; base += 256) {
-    const size_t idx = base + tid;
-    const bool in = idx < end;
-    const float sv = in ? s[idx] : -INFINITY;
-    const uint32_t key = order_key(sv);
-    const bool match = in && (key & hi_mask) == S.prefix;
-    const uint32_t dg = (key >> shift) & 0xffu;
-    histogram_add(cnt, mass, match, dg, match ? pool_mass(sv, m, unit) : 0ull);
+  // four coalesced loads in flight per thread before any is used (the counts and the
+  // fixed-point masses are integers, so the order of the additions does not matter)
+  constexpr int U = 4;
+  for (size_t base = begin; base < end; base += U * 256) {
+    float sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t idx = base + u * 256 + tid;
+      sv[u] = idx < end ? s[idx] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = base + u * 256 + tid < end;
+      const uint32_t key = order_key(sv[u]);
+      const bool match = in && (key & hi_mask) == S.prefix;
+      const uint32_t dg = (key >> shift) & 0xffu;
+      histogram_add(cnt, mass, match, dg, match ? pool_mass(sv[u], m, unit) : 0ull);
+    }
   }
   __syncthreads();
   if (cnt[tid]) {
