@@ -633,26 +633,40 @@ __global__ void pool_max_kernel(int N, const float* __restrict__ scores,
   if ((threadIdx.x & 63) == 0) atomicMax(&st[grp].mkey, order_key(mx));
 }
 
+constexpr int kScoreTiles = 3;   // tiles of 32 key blocks per wave of token_scores_kernel
+
 template <int D, typename T>
 __global__ __launch_bounds__(64) void token_scores_kernel(Geom g, const T* __restrict__ q,
                                                           const float* __restrict__ kp,
                                                           float* __restrict__ scores,
                                                           PoolState* __restrict__ st,
                                                           float scale) {
+  // one wave: 32 tokens against kScoreTiles tiles of 32 blocks; each Q fragment feeds the
+  // tiles' independent product chains (each tile's chain is the same as alone)
+  constexpr int JT = kScoreTiles;
   const int lane = threadIdx.x;
-  const int x0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const int x0 = blockIdx.x * 32, j00 = blockIdx.y * 32 * JT;
   const int grp = blockIdx.z;
   const int half = lane >> 5;
-  const int rx = x0 + (lane & 31), rj = j0 + (lane & 31);
+  const int rx = x0 + (lane & 31);
   const int b = grp / g.Hh, h = grp - b * g.Hh;
   const T* qrow = q + ((size_t(b) * g.L + min(rx, g.L - 1)) * g.Hh + h) * D + half * (D / 2);
-  const float* krow = kp + (size_t(grp) * g.Nb + min(rj, g.Nb - 1)) * D + half * (D / 2);
-  const bool qok = rx < g.L, kok = rj < g.Nb;
-  f32x16_t acc;
+  const bool qok = rx < g.L;
+  const float* krow[JT];
+  bool kok[JT];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int jt = 0; jt < JT; ++jt) {
+    const int rj = j00 + jt * 32 + (lane & 31);
+    kok[jt] = rj < g.Nb;
+    krow[jt] = kp + (size_t(grp) * g.Nb + min(rj, g.Nb - 1)) * D + half * (D / 2);
+  }
+  f32x16_t acc[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[jt][v] = 0.f;
   // lane half `half` feeds d in [half*D/2, (half+1)*D/2) for both operands
-#pragma unroll 4
+#pragma unroll 2
   for (int c = 0; c < D / 2; c += 4) {
     float4 a;
     if constexpr (sizeof(T) == 2) {
@@ -662,24 +676,36 @@ __global__ __launch_bounds__(64) void token_scores_kernel(Geom g, const T* __res
     } else {
       a = *reinterpret_cast<const float4*>(qrow + c);
     }
-    float4 bb = *reinterpret_cast<const float4*>(krow + c);
     if (!qok) a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!kok) bb = make_float4(0.f, 0.f, 0.f, 0.f);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bb.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bb.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bb.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bb.w, acc, 0, 0, 0);
-  }
-  // acc[v]: token x0 + 8*(v/4) + 4*half + v%4, block j0 + lane%32
-  float mx = -INFINITY;
-  if (kok) {
+    float4 bb[JT];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int x = x0 + 8 * (v >> 2) + 4 * half + (v & 3);
-      if (x < g.L) {
-        const float sv = acc[v] * scale;
-        scores[(size_t(grp) * g.L + x) * g.Nb + rj] = sv;
-        mx = fmaxf(mx, sv);
+    for (int jt = 0; jt < JT; ++jt) {
+      bb[jt] = *reinterpret_cast<const float4*>(krow[jt] + c);
+      if (!kok[jt]) bb[jt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, bb[jt].x, acc[jt], 0, 0, 0);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, bb[jt].y, acc[jt], 0, 0, 0);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, bb[jt].z, acc[jt], 0, 0, 0);
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[jt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, bb[jt].w, acc[jt], 0, 0, 0);
+  }
+  // acc[jt][v]: token x0 + 8*(v/4) + 4*half + v%4, block j00 + 32 jt + lane%32
+  float mx = -INFINITY;
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) {
+    if (kok[jt]) {
+      const int rj = j00 + jt * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int x = x0 + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (x < g.L) {
+          const float sv = acc[jt][v] * scale;
+          scores[(size_t(grp) * g.L + x) * g.Nb + rj] = sv;
+          mx = fmaxf(mx, sv);
+        }
       }
     }
   }
@@ -1172,7 +1198,7 @@ int launch_select_tokens(const Geom& g, const void* q, const float* k_pool, floa
   fill_zero_kernel<<<64, 256, 0, st>>>(reinterpret_cast<uint32_t*>(w.state), zero_words);
   fill_zero_kernel<<<1024, 256, 0, st>>>(w.qbits, size_t(G) * g.Nb * W);
   const float scale = 1.0f / sqrtf(float(g.D));
-  const dim3 sgrid((g.L + 31) / 32, (g.Nb + 31) / 32, G);
+  const dim3 sgrid((g.L + 31) / 32, ((g.Nb + 31) / 32 + kScoreTiles - 1) / kScoreTiles, G);
   if (g.D == 128)
     token_scores_kernel<128, uint16_t><<<sgrid, 64, 0, st>>>(
         g, static_cast<const uint16_t*>(q), k_pool, w.scores, w.state, scale);
