@@ -69,7 +69,13 @@ __device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
 // Sum over the 64 lanes of a wave, returned to every lane, without going through LDS:
 // DPP swaps inside quads (lane ^ 1, ^ 2), then mirrors inside half rows and rows of 16,
 // then the swaps of rows 0/1 with 2/3... (lane ^ 16) and of the two halves (lane ^ 32).
+// Precondition: all 64 lanes are active.  The DPP moves (bound_ctrl off) and the permlane
+// swaps read the registers of inactive lanes as they stand, so a call from divergent code
+// would add stale values.  Builds with VMOBA_DEVICE_CHECKS trap on a partial wave.
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#ifdef VMOBA_DEVICE_CHECKS
+  if (__builtin_amdgcn_read_exec() != ~0ull) __builtin_trap();
+#endif
   v += dpp_u64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
   v += dpp_u64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
   v += dpp_u64<0x141>(v);   // row_half_mirror

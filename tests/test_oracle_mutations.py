@@ -181,3 +181,17 @@ def test_token_forced_pair_of_wrong_block_is_caught(monkeypatch):
     assert not _fails(t_tok.test_prefix_invariants, 1)
     monkeypatch.setattr(otok, "token_select", wrong_diag)
     assert _fails(t_tok.test_prefix_invariants, 1)
+
+
+def test_token_pool_temperature_slip_is_caught(monkeypatch):
+    """A scale inside the token-pool softmax still sums to one; the scipy pin sees it."""
+    import test_oracle_tokens as t_tok
+    from oracle import tokens as otok
+    orig = otok.normalise_token_pool
+
+    def hot(s):
+        return orig(np.asarray(s, float) / 0.9)
+    assert not _fails(t_tok.test_pool_normalisation_is_scipy_softmax_over_flattened_pool)
+    monkeypatch.setattr(otok, "normalise_token_pool", hot)
+    assert not _fails(t_tok.test_pool_normalisation_sums_to_one)
+    assert _fails(t_tok.test_pool_normalisation_is_scipy_softmax_over_flattened_pool)

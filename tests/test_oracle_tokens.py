@@ -2,7 +2,8 @@
 
 - scores: the token-to-block score equals the mean of the token-to-token scores over the
   key block (by linearity of the block mean), computed here by explicit loops;
-- normalisation: every head's pool sums to one;
+- normalisation: every head's pool sums to one, and equals scipy's softmax over the
+  head's flattened L * N_b pool (shift-invariant per head, heads independent);
 - threshold: brute force over every subset of a 16-entry pool finds the same minimal
   count; minimality, the ceil(tau L N_b) bound and nestedness in tau; a hand-worked
   example whose cut falls inside a run of equal values (ties by ascending index);
@@ -53,6 +54,27 @@ def test_pool_normalisation_sums_to_one():
     shat = otok.normalise_token_pool(otok.token_scores(q, oracle.block_means(k, mem)))
     assert (shat >= 0).all()
     assert np.abs(shat.sum(axis=(2, 3)) - 1.0).max() <= 1e-12
+
+
+def test_pool_normalisation_is_scipy_softmax_over_flattened_pool():
+    """Against scipy's softmax over each head's L * N_b entries (a library routine): a
+    temperature, a scale, a per-row or per-column normaliser or a mixed-up head would
+    each differ.  Scores spread over [-40, 40] so exp without the max shift overflows
+    nowhere but a wrong scale is far off."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(3)
+    B, Hh, L, nb = 2, 3, 12, 5
+    s = rng.uniform(-40.0, 40.0, (B, Hh, L, nb))
+    s[1, 2] *= 0.01                       # one nearly uniform head
+    got = otok.normalise_token_pool(s)
+    want = softmax(s.reshape(B, Hh, L * nb), axis=-1).reshape(B, Hh, L, nb)
+    assert np.abs(got - want).max() <= 1e-14
+    assert np.abs(got[1, 2] - 1.0 / (L * nb)).max() <= 0.5 / (L * nb)
+    # shift invariance per head, and no coupling between heads
+    s2 = s.copy()
+    s2[0, 1] += 123.0
+    got2 = otok.normalise_token_pool(s2)
+    assert np.abs(got2 - got).max() <= 1e-14
 
 
 @pytest.mark.parametrize("tau", [0.1, 0.25, 0.5, 0.8])
