@@ -10,6 +10,14 @@ forward -> backward (delta, dK/dV, dQ).  The default workload is the 3D layer at
 Prints one JSON line.  value = algorithmic TFLOP/s over the selected pairs,
 (4 + 8) * d * P per step with P the selected token pairs (forward: Q K^T and P V;
 backward: dV, dP, dQ, dK), divided by the measured step time.
+
+Timing: W untimed warm-up steps, then K steps between two device synchronisations
+(ms_per_step, the mean of the wall time, which gives `value`), with HIP events around
+every stage of every step on the launch stream (stage means for the roofline, medians in
+`timing`).  Then, unless --no-flush, the same K steps again, each after a 512 MiB scratch
+write that evicts the L2 caches and the Infinity Cache (medians in `timing`, suffix
+_flushed).  Then, unless --no-clock, 1.5 s of back-to-back steps while a second thread
+samples the shader clock; `sclk` holds its median and the bf16 peak scaled to it.
 """
 
 import argparse
@@ -24,13 +32,19 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_SCLK_MHZ = 2400.0      # the shader clock the bf16 peak is quoted at
+FLUSH_BYTES = 512 << 20     # scratch written before each flushed repeat
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the repeats with a 512 MiB scratch write before each step")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock during a 1.5 s run of steps")
     ap.add_argument("--workload", default="l3d_55k")
     ap.add_argument("--layer", type=int, default=0, help="layer of the workload's cycle")
     ap.add_argument("--tau", type=float, default=None)
@@ -95,9 +109,12 @@ def cpu_baseline(inp, cfg, spec, tau, min_seconds=10.0, max_heads=4, mode="thres
         flops += 12.0 * cfg["head_dim"] * float(mask.sum()) * S * S
         heads += 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"heads 0-{heads - 1} of {cfg['heads']} of the same layer (pool, select, "
-                      f"sparse fwd+bwd in fp64), {dt:.1f} s wall, {flops / 1e12:.3f} TFLOP "
-                      f"algorithmic", "seconds": dt}
+            "sample": f"whole heads 0-{heads - 1} of {cfg['heads']} of the same layer (pool, "
+                      f"select, sparse fwd+bwd in fp64): {dt:.1f} s wall for "
+                      f"{flops / 1e12:.3f} TFLOP algorithmic; the rate is extrapolated to "
+                      f"the layer's other heads (heads are independent problems of "
+                      f"similar size)",
+            "heads_timed": heads, "heads_in_layer": cfg["heads"], "seconds": dt}
 
 
 def _kernel_source_hash(kernel):
@@ -162,8 +179,58 @@ def dq_kernel_name(qlim, head_dim, bf16):
     return "attn_bwd_dq_bf16_kernel"
 
 
+def _event_medians(evs, names, suffix):
+    """Median over repeats of the step time and of each stage (HIP events)."""
+    import statistics
+    n = len(names)
+    step = [e[0].elapsed_time(e[n]) for e in evs]
+    stages = {nm: round(statistics.median(e[j].elapsed_time(e[j + 1]) for e in evs), 4)
+              for j, nm in enumerate(names)}
+    return {f"ms_per_step_median{suffix}": round(statistics.median(step), 4),
+            f"ms_per_step_min{suffix}": round(min(step), 4),
+            f"stage_ms_median{suffix}": stages}
+
+
+def sample_sclk(step, seconds=1.5):
+    """Shader clock (MHz, amd-smi's current GFX clock through torch) sampled every 10 ms
+    from a second thread while `step` runs back to back for `seconds`."""
+    import statistics
+    import threading
+    import torch
+    try:
+        torch.cuda.clock_rate(0)
+    except Exception as e:   # no amd-smi access on this host
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                c = torch.cuda.clock_rate(0)
+                if c:
+                    samples.append(float(c))
+            except Exception:
+                pass
+            time.sleep(0.01)
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return {"error": "no samples"}
+    med = statistics.median(samples)
+    return {"median_mhz": med, "min_mhz": min(samples), "max_mhz": max(samples),
+            "samples": len(samples), "seconds": seconds,
+            "bf16_peak_at_median_tflops": round(PEAK_BF16_TFLOPS * med / PEAK_SCLK_MHZ, 1)}
+
+
 def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
-               mode="threshold_global", topk=None):
+               mode="threshold_global", topk=None, flush=False, clock=False):
     """Time the hot path of one layer of a workload; returns a dict of measurements.
     mode / topk choose the selection strategy (threshold_global, the method's, by default)."""
     import torch
@@ -216,6 +283,21 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
     stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
                 for j, n in enumerate(names)}
+    timing = {"repeats": steps, "ms_per_step_mean_wall": round(ms_step, 4)}
+    timing.update(_event_medians(evs, names, ""))
+    if flush:
+        # the same steps with a 512 MiB scratch write before each (evicts L2 and the
+        # 256 MB Infinity Cache); events bracket the step only
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(float(i))
+            step(fevs[i])
+        torch.cuda.synchronize()
+        del scratch
+        timing["flush_bytes"] = FLUSH_BYTES
+        timing.update(_event_medians(fevs, names, "_flushed"))
+    sclk = sample_sclk(step) if clock else None
 
     nnz = float(sel.head_stats[:, 1].double().sum().item())
     pairs = nnz * S * S
@@ -249,7 +331,7 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
                 ms_step=ms_step, stage_ms=stage_ms, pairs=pairs,
                 density=nnz / (p.groups * nb * nb), fl=fl, executed=executed,
                 pool_bytes=pool_bytes, select_bytes=select_bytes, kernel_names=kernel_names,
-                dense=dense, cpu=cpu)
+                dense=dense, cpu=cpu, timing=timing, sclk=sclk)
 
 
 def run_tokens(workload, layer, tau, steps, warmup):
@@ -461,7 +543,8 @@ def main():
 
     r = run_config(args.workload, args.layer, args.tau, args.steps, args.warmup,
                    0 if args.no_dense else 2, not args.no_cpu_baseline,
-                   args.select_mode, args.topk)
+                   args.select_mode, args.topk, flush=not args.no_flush,
+                   clock=not args.no_clock)
     ms_step, stage_ms, fl = r["ms_step"], r["stage_ms"], r["fl"]
     value = 12.0 * r["d"] * r["pairs"] / (ms_step * 1e-3) / 1e12
     dom = max(["fwd", "dkdv", "dq"], key=lambda n: stage_ms[n])
@@ -499,7 +582,14 @@ def main():
             "executed_flops_per_launch": r["executed"][dom],
             "mfma_util_counter": None if mfma_util is None else round(mfma_util, 4)},
         "cpu_baseline": r["cpu"],
+        "timing": r["timing"],
+        "sclk": r["sclk"],
     }
+    sc = r["sclk"]
+    if sc and "median_mhz" in sc:
+        # the same work against the peak at the clock the chip held while running it
+        line["roofline"]["peak_at_sclk"] = sc["bf16_peak_at_median_tflops"]
+        line["roofline"]["frac_at_sclk"] = round(achieved / sc["bf16_peak_at_median_tflops"], 4)
     line.update(summary(r))
     print(json.dumps(line), flush=True)
 

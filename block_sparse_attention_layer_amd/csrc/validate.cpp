@@ -22,14 +22,19 @@ int validate_problem(const vmoba_problem* p) {
   const int mode = p->layer_idx % 3;
   if (mode == 0 && (p->bh != p->H || p->bw != p->W)) return VMOBA_ERR_MODE;
   if (mode == 1 && p->bt != p->T) return VMOBA_ERR_MODE;
-  // Every element count and index used on the device stays below 2^31.
-  const int64_t L = int64_t(p->T) * p->H * p->W;
-  const int64_t elems = int64_t(p->batch) * L * p->heads * p->head_dim;
-  const int64_t nb = (int64_t(p->T) / p->bt) * (p->H / p->bh) * (p->W / p->bw);
-  const int64_t groups = int64_t(p->batch) * p->heads;
-  if (L >= (int64_t(1) << 31) || elems >= (int64_t(1) << 31) ||
-      groups * L >= (int64_t(1) << 31) || groups * nb * nb >= (int64_t(1) << 31) ||
-      nb * nb >= (int64_t(1) << 31))
+  // Every element count and index used on the device stays below 2^31.  The products are
+  // formed with a saturating multiply (all factors are positive here), so no intermediate
+  // overflows whatever the sizes.
+  constexpr int64_t kLim = int64_t(1) << 31;
+  auto mul = [](int64_t a, int64_t b) -> int64_t {
+    return a >= kLim || b >= kLim || a * b >= kLim ? kLim : a * b;
+  };
+  const int64_t L = mul(mul(p->T, p->H), p->W);
+  const int64_t elems = mul(mul(mul(p->batch, L), p->heads), p->head_dim);
+  const int64_t nb = mul(mul(p->T / p->bt, p->H / p->bh), p->W / p->bw);
+  const int64_t groups = mul(p->batch, p->heads);
+  if (L >= kLim || elems >= kLim || mul(groups, L) >= kLim ||
+      mul(mul(groups, nb), nb) >= kLim || mul(nb, nb) >= kLim)
     return VMOBA_ERR_OVERFLOW;
   return VMOBA_OK;
 }

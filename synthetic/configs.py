@@ -14,7 +14,8 @@ class LayerSpec:
     block: Tuple[int, int, int]
 
 
-CONFIG_ORDER = ["tiny", "l1d_32k", "l2d_32k", "l3d_55k", "cycle_76k", "blocks_55k"]
+CONFIG_ORDER = ["tiny", "l1d_32k", "l2d_32k", "l3d_55k", "cycle_76k", "blocks_55k",
+                "blocks_46k", "blocks_11k"]
 
 CONFIGS = {
     # 256 tokens, fp32, 2 heads of 64, 3D blocks (2,4,4): 8 blocks of 32 tokens.
@@ -46,6 +47,21 @@ CONFIGS = {
     "blocks_55k": dict(batch=1, heads=12, head_dim=128, T=24, H=36, W=64,
                        layers=(LayerSpec(0, (3, 36, 64)), LayerSpec(1, (24, 6, 8)),
                                LayerSpec(2, (8, 12, 8))),
+                       taus=(0.25,), dtype="bf16", backward=True, field="smooth"),
+    # The pre-training setting "10-48-60" of paperlayer App. C (Table 6): 1D/2D/3D block
+    # counts 10, 48 and 60 at 46K and 11K tokens, tau 0.25.  The pages give no latent shape
+    # for either length; these are factorisations with a frame count divisible by 10.
+    # 46,080 tokens = 20x36x64: 1D blocks of 2 frames (10 of 4,608), 2D patches of 6x8
+    # across all frames (48 of 960), 3D blocks (4,12,16) (5x3x4 = 60 of 768).
+    "blocks_46k": dict(batch=1, heads=12, head_dim=128, T=20, H=36, W=64,
+                       layers=(LayerSpec(0, (2, 36, 64)), LayerSpec(1, (20, 6, 8)),
+                               LayerSpec(2, (4, 12, 16))),
+                       taus=(0.25,), dtype="bf16", backward=True, field="smooth"),
+    # 11,520 tokens = 10x24x48: 1D blocks of one frame (10 of 1,152), 2D patches of 4x6
+    # across all frames (48 of 240), 3D blocks (2,8,12) (5x3x4 = 60 of 192).
+    "blocks_11k": dict(batch=1, heads=12, head_dim=128, T=10, H=24, W=48,
+                       layers=(LayerSpec(0, (1, 24, 48)), LayerSpec(1, (10, 4, 6)),
+                               LayerSpec(2, (2, 8, 12))),
                        taus=(0.25,), dtype="bf16", backward=True, field="smooth"),
 }
 

@@ -3,7 +3,8 @@
 * libvmoba.so loads and exports every function include/vmoba.h declares;
 * every argument error is reported before anything is enqueued;
 * the fast division and the partition arithmetic of the kernels' geometry header
-  agree with exact division and with the oracle's block table.
+  agree with exact division and with the oracle's block table;
+* the host code runs clean under the address and undefined-behaviour sanitizers.
 """
 
 import ctypes
@@ -189,6 +190,30 @@ def test_kernel_token_map_matches_oracle_blocks(geom_exe, lat, block):
     got = np.array(out.split(), dtype=np.int64)
     ref = oracle.block_members(*lat, block).reshape(-1)
     assert np.array_equal(got, ref)
+
+
+SANITIZE_DIR = os.path.join(ROOT, "tests", "host_sanitize")
+CSRC = os.path.join(ROOT, "block_sparse_attention_layer_amd", "csrc")
+
+
+def test_host_code_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """api.cpp and validate.cpp built by g++ with ASan and UBSan (aborting on the first
+    report), linked against host stand-ins of the kernel launchers: every entry point with
+    valid arguments and with each argument error, every op's workspace size, every status
+    string, sizes near and far past the int32 limits, and the geometry helpers."""
+    exe = tmp_path / "vmoba_host_sanitized"
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer"]
+    cmd = ["g++", "-std=c++17", "-g", "-O1", *san, "-I", os.path.join(ROOT, "include"),
+           os.path.join(SANITIZE_DIR, "driver.cpp"),
+           os.path.join(SANITIZE_DIR, "stub_launchers.cpp"),
+           os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "validate.cpp"), "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok")
 
 
 def test_select_mode_errors(L):

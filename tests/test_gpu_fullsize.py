@@ -25,7 +25,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = 2e-2
 
-LAYERS = [(name, li) for name in ("l1d_32k", "l2d_32k", "l3d_55k", "cycle_76k", "blocks_55k")
+LAYERS = [(name, li) for name in ("l1d_32k", "l2d_32k", "l3d_55k", "cycle_76k", "blocks_55k",
+                                  "blocks_46k", "blocks_11k")
           for li, _ in config_layers(name)]
 
 
