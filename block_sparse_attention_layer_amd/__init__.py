@@ -9,6 +9,7 @@ from .api import (Problem, Selection, TokenSelection, vmoba_select_tokens,
                   vmoba_dense_attn_bwd, vmoba_dense_attn_fwd,
                   vmoba_num_blocks, vmoba_partition_pool, vmoba_select,
                   vmoba_sparse_attn_bwd, vmoba_sparse_attn_bwd_delta,
+                  vmoba_sparse_attn_bwd_noalloc,
                   vmoba_sparse_attn_bwd_dkdv, vmoba_sparse_attn_bwd_dq,
                   vmoba_sparse_attn_fwd, vmoba_validate,
                   vmoba_workspace_size)
@@ -25,6 +26,7 @@ __all__ = [
     "vmoba_dense_attn_bwd", "vmoba_dense_attn_fwd", "vmoba_num_blocks",
     "vmoba_partition_pool", "vmoba_select", "vmoba_sparse_attn_bwd",
     "vmoba_sparse_attn_bwd_delta", "vmoba_sparse_attn_bwd_dkdv", "vmoba_sparse_attn_bwd_dq",
+    "vmoba_sparse_attn_bwd_noalloc",
     "vmoba_sparse_attn_fwd", "vmoba_validate", "vmoba_workspace_size",
     "vmoba_select_tokens", "vmoba_token_attn_fwd", "vmoba_token_attn_bwd",
 ]

@@ -15,8 +15,9 @@ STATUS_NAMES = {
     0: "VMOBA_OK", 1: "VMOBA_ERR_NULL", 2: "VMOBA_ERR_SHAPE", 3: "VMOBA_ERR_MODE",
     4: "VMOBA_ERR_TAU", 5: "VMOBA_ERR_DTYPE", 6: "VMOBA_ERR_HEAD_DIM",
     7: "VMOBA_ERR_WORKSPACE", 8: "VMOBA_ERR_OVERFLOW", 9: "VMOBA_ERR_HIP",
-    10: "VMOBA_ERR_OP", 11: "VMOBA_ERR_SELECT",
+    10: "VMOBA_ERR_OP", 11: "VMOBA_ERR_SELECT", 12: "VMOBA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 16 << 20   # VMOBA_NOALLOC_SCRATCH_BYTES
 VMOBA_BF16, VMOBA_FP32 = 0, 1
 OPS = {"pool": 0, "select": 1, "sparse_fwd": 2, "sparse_bwd": 3, "dense_fwd": 4,
        "dense_bwd": 5, "select_tokens": 6, "token_fwd": 7, "token_bwd": 8}
@@ -47,6 +48,7 @@ _SIG = {
                                              _P, _P, _P, ctypes.c_size_t, _P]),
     "vmoba_sparse_attn_bwd": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 14 +
                               [ctypes.c_size_t, _P]),
+    "vmoba_sparse_attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 14),
     "vmoba_sparse_attn_bwd_delta": (ctypes.c_int, [ctypes.POINTER(CProblem), _P, _P, _P, _P]),
     "vmoba_sparse_attn_bwd_dkdv": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 11),
     "vmoba_sparse_attn_bwd_dq": (ctypes.c_int, [ctypes.POINTER(CProblem)] + [_P] * 10),

@@ -221,6 +221,29 @@ def vmoba_sparse_attn_bwd(p: Problem, q, k, v, o, lse, dout, row_ptr, col_idx, c
     return tuple(outs)
 
 
+def vmoba_sparse_attn_bwd_noalloc(p: Problem, q, k, v, o, lse, dout, row_ptr, col_idx,
+                                  col_ptr, row_idx, dq, dk, dv):
+    """vmoba_sparse_attn_bwd into caller-allocated dq, dk, dv with no workspace: the
+    library keeps delta in a fixed per-GPU device array, and this call allocates nothing."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _want(t, name, _tok_shape(p), p.dtype, dev)
+    _want(lse, "lse", (p.batch, p.heads, p.L), torch.float32, dev)
+    _check_lists(p, dev, ("row_ptr", row_ptr, lambda n: n + 1),
+                 ("col_idx", col_idx, lambda n: n * n),
+                 ("col_ptr", col_ptr, lambda n: n + 1),
+                 ("row_idx", row_idx, lambda n: n * n))
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, _tok_shape(p), p.gdtype, dev)
+    s = p.c_struct()
+    check(lib().vmoba_sparse_attn_bwd_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(o), _ptr(lse), _ptr(dout), _ptr(row_ptr),
+                                              _ptr(col_idx), _ptr(col_ptr), _ptr(row_idx),
+                                              _ptr(dq), _ptr(dk), _ptr(dv), _stream(dev)),
+          "vmoba_sparse_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
 def vmoba_sparse_attn_bwd_delta(p: Problem, o, dout, delta=None):
     dev = o.device
     _want(o, "o", _tok_shape(p), p.dtype, dev)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvmoba.so")
 
-HIP_SOURCES = ["pool.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip"]
+HIP_SOURCES = ["pool.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "noalloc.hip"]
 HOST_SOURCES = ["validate.cpp", "api.cpp"]
 
 ARCH = "gfx950"

@@ -124,6 +124,7 @@ const char* vmoba_status_string(int status) {
     case VMOBA_ERR_HIP: return "HIP runtime error";
     case VMOBA_ERR_OP: return "unknown op";
     case VMOBA_ERR_SELECT: return "unknown selection mode or top-k count < 1";
+    case VMOBA_ERR_SCRATCH: return "problem needs more delta rows than the no-allocation backward's fixed scratch holds (B * Hh * L * 4 bytes > VMOBA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -62,7 +62,8 @@ typedef enum {
   VMOBA_ERR_OVERFLOW = 8,   /* an index or element count exceeds the int32 range used  */
   VMOBA_ERR_HIP = 9,        /* the HIP runtime reported an error at launch             */
   VMOBA_ERR_OP = 10,        /* unknown op in vmoba_workspace_size                      */
-  VMOBA_ERR_SELECT = 11     /* unknown selection mode, or top-k count k < 1            */
+  VMOBA_ERR_SELECT = 11,    /* unknown selection mode, or top-k count k < 1            */
+  VMOBA_ERR_SCRATCH = 12    /* problem needs more than the fixed no-allocation scratch */
 } vmoba_status;
 
 typedef enum { VMOBA_BF16 = 0, VMOBA_FP32 = 1 } vmoba_dtype;
@@ -196,6 +197,26 @@ int vmoba_sparse_attn_bwd_dq(const vmoba_problem* p, const void* q, const void* 
                              const void* v, const float* lse, const float* delta,
                              const void* dout, const int32_t* row_ptr,
                              const int32_t* col_idx, void* dq, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that forbid hipMalloc): vmoba_sparse_attn_bwd with no workspace argument.  Same
+ * arguments, results and kernels as vmoba_sparse_attn_bwd.  Its one scratch buffer, delta
+ * (fp32 [B][Hh][L]), is a fixed device array of VMOBA_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends; the call allocates nothing.
+ * B * Hh * L * 4 > VMOBA_NOALLOC_SCRATCH_BYTES is rejected with VMOBA_ERR_SCRATCH before
+ * anything is enqueued (16 MiB: up to 4,194,304 rows, e.g. 12 heads at 349,525 tokens).
+ * The first call on a device looks the array's device address up (a runtime query, with
+ * that device made current for the lookup); the stream's device is the one used.  Every
+ * call on one GPU shares that GPU's array: each call rewrites it in full before reading
+ * it, but calls that overlap in time on one GPU (e.g. on two streams) race on it. */
+#define VMOBA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int vmoba_sparse_attn_bwd_noalloc(const vmoba_problem* p, const void* q, const void* k,
+                                  const void* v, const void* o, const float* lse,
+                                  const void* dout, const int32_t* row_ptr,
+                                  const int32_t* col_idx, const int32_t* col_ptr,
+                                  const int32_t* row_idx, void* dq, void* dk, void* dv,
+                                  void* stream);
 
 /* Token-granular selection: papernotes 关键设计 2 read with q_i all of the head's query
  * tokens (s x d) instead of block means.  The pool of a head group is every (query token

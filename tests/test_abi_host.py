@@ -106,6 +106,26 @@ def test_null_and_tau_and_workspace_errors(L):
                                    FAKE, FAKE, 1 << 30, NULL) == 2
 
 
+def test_noalloc_backward_host_errors(L):
+    """The no-allocation backward rejects, before any HIP call: a bad problem, NULL
+    pointers, too many blocks, and a problem whose delta rows exceed its fixed scratch."""
+    bp = ctypes.byref(_prob())
+    assert L.vmoba_sparse_attn_bwd_noalloc(ctypes.byref(_prob(T=5)), *([FAKE] * 13), NULL) == 2
+    for i in range(13):
+        args = [FAKE] * 13
+        args[i] = NULL
+        assert L.vmoba_sparse_attn_bwd_noalloc(bp, *args, NULL) == 1
+    many = _prob(T=1, H=1, W=1025, bt=1, bh=1, bw=1, layer_idx=2)
+    assert L.vmoba_sparse_attn_bwd_noalloc(ctypes.byref(many), *([FAKE] * 13), NULL) == 2
+    # 8 x 12 heads x 75,600 tokens of fp32 delta = 29 MB > 16 MiB
+    big = _prob(batch=8, heads=12, head_dim=128, T=21, H=45, W=80, bt=3, bh=9, bw=8,
+                dtype=0, grad_dtype=0)
+    assert L.vmoba_validate(ctypes.byref(big)) == 0
+    assert 8 * 12 * 75600 * 4 > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.vmoba_sparse_attn_bwd_noalloc(ctypes.byref(big), *([FAKE] * 13), NULL) == 12
+    assert b"scratch" in L.vmoba_status_string(12)
+
+
 def test_too_many_blocks_rejected_by_sparse_calls(L):
     # 1025 blocks of one token: above the selection kernel's limit
     p = _prob(T=1, H=1, W=1025, bt=1, bh=1, bw=1, layer_idx=2)
