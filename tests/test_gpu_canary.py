@@ -114,6 +114,9 @@ def test_outputs_and_workspaces_stay_in_bounds(case):
     check(L.vmoba_sparse_attn_bwd(sp, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(do), _p(rp),
                                   _p(ci), _p(cp), _p(ri), _p(dq), _p(dk), _p(dv), _p(wsb),
                                   nb_ws, _stream()), "sparse bwd")
+    check(L.vmoba_sparse_attn_bwd_noalloc(sp, _p(q), _p(k), _p(v), _p(o), _p(lse), _p(do),
+                                          _p(rp), _p(ci), _p(cp), _p(ri), _p(dq), _p(dk),
+                                          _p(dv), _stream()), "no-alloc bwd")
     od, lsed = c.view(tok, bf), c.view((batch, heads, p.L), f32)
     check(L.vmoba_dense_attn_fwd(sp, _p(q), _p(k), _p(v), _p(od), _p(lsed),
                                  ctypes.c_void_p(0), 0, _stream()), "dense fwd")
