@@ -973,20 +973,33 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
       }
       bh = (li0 + 1) * g.S - t * KT - 4 * g16;
     }
+    float pv[2][M][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float pv[4];
+      for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
-          if (ragged && t * KT + ks * 16 + 4 * g16 + i >= nkeys) pv[i] = 0.f;
-          if constexpr (TOK) pv[i] = ((ks * 16 + i) < bh ? b0[m] : b1[m]) ? pv[i] : 0.f;
+          pv[ks][m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
+          if constexpr (TOK) pv[ks][m][i] = ((ks * 16 + i) < bh ? b0[m] : b1[m]) ? pv[ks][m][i] : 0.f;
         }
+    // the ragged last tile only (a uniform branch, so the other tiles pay no selects)
+    if (ragged) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t * KT + ks * 16 + 4 * g16 + i >= nkeys) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) pv[ks][m][i] = 0.f;
+          }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < M; ++m)
         *reinterpret_cast<float4*>(xb + ((ks * M + m) * 64 + lane) * 4) =
-            float4{pv[0], pv[1], pv[2], pv[3]};
-      }
+            float4{pv[ks][m][0], pv[ks][m][1], pv[ks][m][2], pv[ks][m][3]};
   };
   // role dQ: dS^T of the previous tile (P in xb, dP in dprev), packed as B operands
   auto finish_ds = [&](const float* xb, const Acc& dprev, bf16x8 (&sbf)[M])

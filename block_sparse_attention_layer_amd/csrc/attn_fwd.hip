@@ -418,19 +418,13 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   static_assert(NS == 4, "the step loop is unrolled over four stages");
   constexpr float kRescaleLog2 = 8.0f;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stages[NS * 2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
   auto stage = [&](auto Ic) -> unsigned char* {
     constexpr int I = decltype(Ic)::value % NS;
-    if constexpr (I == 0) return stage0;
-    else if constexpr (I == 1) return stage1;
-    else if constexpr (I == 2) return stage2;
-    else return stage3;
+    return stages + I * (2 * TILE);
   };
 
   const Geom& g = a.g;
@@ -458,6 +452,7 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // w, known to be wave-uniform
   const int g16 = lane >> 4, i16 = lane & 15;
 
   int nkeys;
@@ -534,7 +529,7 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   auto issue_offsets = [&](const int32_t (&o)[LPW], unsigned char* smem) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int dst = (w * (KT / NW) + i * 4) * ROWB;   // wave-uniform
+      const int dst = (wu * (KT / NW) + i * 4) * ROWB;   // wave-uniform
       load_to_lds16(rK, 2u * uint32_t(o[i] + kchunk[i]), smem + dst);
       load_to_lds16(rV, 2u * uint32_t(o[i] + vchunk[i]), smem + TILE + dst);
     }
@@ -554,6 +549,15 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   const int vsw = 2 * (vrow & 7);
   const int vc = (i16 & 3) >> 1;
 
+  // per-lane LDS offsets inside a stage, formed once: K fragment of d-step s (key sub-tile
+  // 0; sub-tile 1 is 16 rows further), V^T read of d-tile ds (keys 0..15; +16 rows for keys
+  // 16..31).  The stage and sub-tile parts are constants of each unrolled step.
+  int koff[D / 32], voff[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) koff[s] = krd + 16 * ((4 * s + g16) ^ i16);
+#pragma unroll
+  for (int ds = 0; ds < D / 16; ++ds) voff[ds] = vrd + 16 * ((2 * ds + vc) ^ vsw);
+
   const float c2 = a.scale_log2;
   const float thr = kRescaleLog2 / c2;
 
@@ -563,28 +567,27 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int m = 0; m < M; ++m) sacc[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 ka[2][D / 32];   // the tile's K fragments, read ahead of their products
+    // the K fragments of one 16-key sub-tile at a time, read ahead of its products (the
+    // second sub-tile's reads overlap the first one's products)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 ka[D / 32];
 #pragma unroll
       for (int s = 0; s < D / 32; ++s)
-        ka[ks][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            sm + ks * 16 * ROWB + krd + 16 * ((4 * s + g16) ^ i16)));
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+        ka[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(sm + ks * 16 * ROWB + koff[s]));
 #pragma unroll
       for (int s = 0; s < D / 32; ++s)
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks][s], qf[m][s], sacc[ks][m],
+          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qf[m][s], sacc[ks][m],
                                                                 0, 0, 0);
+    }
     // V^T fragments, read here so that their latency hides behind the softmax
     bf16x8 va[D / 16];
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
-      const int o = vrd + 16 * ((2 * ds + vc) ^ vsw);
-      const u32x2 lo = lds_read_tr16(sm + o);
-      const u32x2 hi = lds_read_tr16(sm + o + 16 * ROWB);
+      const u32x2 lo = lds_read_tr16(sm + voff[ds]);
+      const u32x2 hi = lds_read_tr16(sm + 16 * ROWB + voff[ds]);
       va[ds] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
     if (t * KT + KT > nkeys) {   // ragged last tile: keys past the end score -inf
@@ -682,9 +685,9 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  issue_tile(0, stage0);
-  issue_tile(1, stage1);
-  issue_tile(2, stage2);
+  issue_tile(0, stage(std::integral_constant<int, 0>{}));
+  issue_tile(1, stage(std::integral_constant<int, 1>{}));
+  issue_tile(2, stage(std::integral_constant<int, 2>{}));
   tile_offsets(NS - 1, noff);
   int t = 0;
   for (; t + NS <= ntiles; t += NS) {
