@@ -64,6 +64,11 @@ def parse():
                     help="comma-separated workloads for --sweep (default: all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter scale)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write the profiles/ summaries from the rocprofv3 runs under DIR "
+                         "(kt: kernel trace; fetch, write, mops: counter runs of the step; "
+                         "calf, calw: counter runs of --calibrate-copy; sq*: other counter "
+                         "passes); no GPU is used")
     return ap.parse_args()
 
 
@@ -522,8 +527,176 @@ def summary(r):
     }
 
 
+def _short_kernel(name):
+    """'void vmoba::k<unsigned short, 128>(vmoba::Geom, ...)' -> 'k<bf16, 128>'."""
+    n = name.replace("void ", "").replace("vmoba::", "")
+    depth, out = 0, []
+    for ch in n:   # drop the argument list: the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            break
+        out.append(ch)
+    return "".join(out).replace("unsigned short", "bf16").strip()
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def _per_dispatch(dirpath, counter):
+    """Mean per dispatch of `counter` for every kernel of one rocprofv3 --pmc run."""
+    acc = {}
+    for r in _csv_rows(_find(dirpath, "counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        k = _short_kernel(r["Kernel_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_profile(d, workload="l3d_55k", steps=20, warmup=5):
+    """profiles/ summaries from rocprofv3 output directories under d (see --help)."""
+    out_dir = os.path.join(ROOT, "profiles")
+    hot = ["pool_kernel", "block_scores_kernel", "attn_fwd16_bf16_kernel",
+           "attn_fwd_bf16_kernel", "delta_kernel", "attn_bwd_dkdv_split_bf16_kernel",
+           "attn_bwd_dkdv_bf16_kernel", "attn_bwd_dq_split_bf16_kernel",
+           "attn_bwd_dq_bf16_kernel"]
+    bench_cmd = "python3 <repo>/bench.py"
+    pmc_cmd = ("python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-dense "
+               "--no-flush --no-clock")
+    # kernel trace: all launches, and the timed launches of the sparse instances
+    stats = _csv_rows(_find(os.path.join(d, "kt"), "kernel_stats.csv"))
+    trace = _csv_rows(_find(os.path.join(d, "kt"), "kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by_kernel = {}
+    for r in trace:
+        k = _short_kernel(r["Kernel_Name"])
+        by_kernel.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    lines = [f"# rocprofv3 kernel trace: 3D layer, 55,296 tokens ({workload}), pool + select + "
+             "sparse fwd + bwd", "",
+             "Command (run from /tmp, with TMPDIR=/tmp; `<repo>` is the repository root):", "",
+             f"    rocprofv3 --kernel-trace --stats -d <out>/kt -o kt --output-format csv -- {bench_cmd}",
+             "", f"bench.py with its defaults: {warmup} warm-up steps, {steps} timed steps, the "
+             f"same {steps} steps after a 512 MiB scratch write each, 1.5 s of steps while the "
+             "clock is sampled, then the dense baseline (1 warm-up + 2 timed forward+backward "
+             "passes) and the CPU oracle sample (host only).  Per-kernel statistics of "
+             "`kt_kernel_stats.csv` (every launch of the run):", "",
+             "| kernel | launches | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:22]:
+        lines.append(f"| {_short_kernel(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
+                     f"{float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    lines += ["", f"Averages over the {steps} timed launches of each sparse instance (launches "
+              f"{warmup + 1} to {warmup + steps} in time order, the ones bench.py times with "
+              "events):", ""]
+    timed = {}
+    for k, ds in by_kernel.items():
+        base = k.split("<")[0]
+        if base in hot and ("false" in k or "<bf16, 128>" in k or base in ("pool_kernel", "block_scores_kernel")):
+            if "true, false" in k and base.startswith("attn"):   # dense instances
+                continue
+            sel = ds[warmup:warmup + steps]
+            if sel:
+                timed[k] = sum(sel) / len(sel)
+                lines.append(f"- {k}: {timed[k]:.4f} ms")
+    with open(os.path.join(out_dir, f"kernel_trace_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # HBM traffic and MFMA work per dispatch
+    fetch, n_f = _per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write, _ = _per_dispatch(os.path.join(d, "write"), "WRITE_SIZE")
+    mops, _ = _per_dispatch(os.path.join(d, "mops"), "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    calf, _ = _per_dispatch(os.path.join(d, "calf"), "FETCH_SIZE")
+    calw, _ = _per_dispatch(os.path.join(d, "calw"), "WRITE_SIZE")
+    copy_bytes = float(1 << 30)
+    cf = copy_bytes / (max(calf.values()) * 1024.0)
+    cw = copy_bytes / (max(calw.values()) * 1024.0)
+    rec = {"workload": workload, "fetch_scale": cf, "write_scale": cw, "kernels": {}}
+    rows = []
+    for k in fetch:
+        base = k.split("<")[0]
+        if base not in hot:
+            continue
+        try:
+            sha = _kernel_source_hash(base)
+        except KeyError:
+            sha = None
+        rb, wb = fetch[k] * 1024.0 * cf, write.get(k, 0.0) * 1024.0 * cw
+        rec["kernels"][k] = {"kernel": base, "fetch_kib": fetch[k], "write_kib": write.get(k, 0.0),
+                             "read_bytes": rb, "write_bytes": wb, "traffic_bytes": rb + wb,
+                             "mfma_mops": mops.get(k, 0.0), "source_sha": sha}
+        rows.append(f"| {k} | {n_f[k]} | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | "
+                    f"{rb / 1e9:.3f} | {wb / 1e9:.3f} | {(rb + wb) / 1e9:.3f} | "
+                    f"{mops.get(k, 0.0):.4g} |")
+    with open(os.path.join(out_dir, f"hbm_traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# HBM traffic per launch: 3D layer, 55,296 tokens ({workload})", "",
+             "Commands (run from /tmp, with TMPDIR=/tmp; `<repo>` is the repository root), one "
+             "counter per run:", ""]
+    for name, ctr, cmd in (("fetch", "FETCH_SIZE", pmc_cmd), ("write", "WRITE_SIZE", pmc_cmd),
+                           ("mops", "SQ_INSTS_VALU_MFMA_MOPS_BF16", pmc_cmd),
+                           ("calf", "FETCH_SIZE", "python3 <repo>/bench.py --calibrate-copy"),
+                           ("calw", "WRITE_SIZE", "python3 <repo>/bench.py --calibrate-copy")):
+        lines.append(f"    rocprofv3 --pmc {ctr} -d <out>/{name} -o {name} --output-format csv -- {cmd}")
+    lines += ["", f"Calibration: a plain device copy of 1 GiB reads {max(calf.values()):.0f} KiB "
+              f"of FETCH_SIZE and {max(calw.values()):.0f} KiB of WRITE_SIZE per dispatch, so "
+              f"bytes = FETCH_SIZE x 1024 x {cf:.3f} and WRITE_SIZE x 1024 x {cw:.3f}.", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | "
+              "traffic GB | MFMA MOPs (512 flop) |", "|---|---|---|---|---|---|---|---|"] + rows
+    lines += ["", "`source_sha` in the JSON beside this file hashes the kernel's source file "
+              "with the two shared headers; bench.py reports `roofline.traffic` only while it "
+              "still matches.", "",
+              "Written by `python3 bench.py --summarize-profile <out>` from the runs above."]
+    with open(os.path.join(out_dir, f"hbm_traffic_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # further counter passes (sq*): every counter of every pass, per dispatch
+    passes = sorted(x for x in os.listdir(d) if x.startswith("sq"))
+    if passes:
+        lines = [f"# Counters of the attention kernels: 3D layer, 55,296 tokens ({workload})", "",
+                 "One rocprofv3 --pmc pass per row group below, each as", "",
+                 f"    rocprofv3 --pmc <counters> -d <out>/<pass> -o <pass> --output-format csv -- {pmc_cmd}",
+                 "", "Values are means per dispatch of the sparse instances, summed over the "
+                 "chip as rocprofv3 reports them (SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_* are in "
+                 "quad-cycles; GRBM_GUI_ACTIVE is summed over the 8 XCDs).", ""]
+        kernels = ["attn_fwd16_bf16_kernel<3, 4, false, true>",
+                   "attn_bwd_dkdv_split_bf16_kernel<false, true, bf16, false>",
+                   "attn_bwd_dq_split_bf16_kernel<false, true, bf16, false>"]
+        lines.append("| pass | counter | " + " | ".join(k.split("<")[0] for k in kernels) + " |")
+        lines.append("|---|---|" + "---|" * len(kernels))
+        for ps in passes:
+            vals = {}
+            for r in _csv_rows(_find(os.path.join(d, ps), "counter_collection.csv")):
+                k = _short_kernel(r["Kernel_Name"])
+                vals.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+            for ctr in sorted({c for c, _ in vals}):
+                cells = []
+                for k in kernels:
+                    v = vals.get((ctr, k))
+                    cells.append(f"{sum(v) / len(v):.4g}" if v else "")
+                lines.append(f"| {ps} | {ctr} | " + " | ".join(cells) + " |")
+        with open(os.path.join(out_dir, f"counters_{workload}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    print(json.dumps({"timed_avg_ms": timed, "traffic_gb": {
+        k: round(v["traffic_bytes"] / 1e9, 3) for k, v in rec["kernels"].items()}}))
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.calibrate_copy:
         calibrate_copy()
         return

@@ -376,7 +376,9 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 //   role P (waves 0-3): S, P, dV^T += dO^T P; writes P (fp32, accumulator layout) to an
 //     LDS exchange buffer;
 //   role dS (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
-//     been published by the step barrier, dS and dK^T += Q^T dS.
+//     been published by the step barrier, dS and dK^T += Q^T dS.  Its dP accumulators
+//     start at -delta of their queries, so the products give dP - delta and dS is one
+//     multiply a value.
 // Each wave holds one accumulator (96 registers a lane) and one of K or V, so two waves
 // fit a SIMD (256 registers each): the SIMD's matrix core alternates between them while
 // each one's vector work (the softmax, or the dS) runs beside the other's products.  One
@@ -572,11 +574,12 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 
   using Acc = f32x4[2][KS];
   // S = Q K^T (role P, rows of the Q tile) or dP = dO V^T (role dS, rows of the dO tile)
-  auto products = [&](const unsigned char* rows, Acc& sacc) __attribute__((always_inline)) {
+  auto products = [&](const unsigned char* rows, Acc& sacc, const f32x4 (&init)[2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) sacc[qs][ks] = init[qs];
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
@@ -616,7 +619,8 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   // registers role dS keeps its dP in)
   auto step_p = [&](const unsigned char* sb, float* xb, Acc& sacc)
       __attribute__((always_inline)) {
-    products(sb, sacc);
+    const f32x4 zero[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    products(sb, sacc, zero);
     const float* lse_s = reinterpret_cast<const float*>(sb + 2 * TILE);
     float pv[2][KS][4];
 #pragma unroll
@@ -650,18 +654,16 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   // dP of the current tile (stage sb) into dprev, then dK^T += Q^T dS
   auto finish_ds = [&](const unsigned char* sbp, const float* xb, const Acc& dprev,
                        bf16x8 (&sbf)[KS]) __attribute__((always_inline)) {
-    const float* dl_s = reinterpret_cast<const float*>(sbp + 2 * TILE) + 64;
+    (void)sbp;
     float sv[2][KS][4];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const float4 d4 = *reinterpret_cast<const float4*>(dl_s + qs * 16 + 4 * g16);
-      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const float4 p4 = *reinterpret_cast<const float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4);
         const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[qs][ks][i] = pv[i] * (dprev[qs][ks][i] - dv4[i]);
+        for (int i = 0; i < 4; ++i) sv[qs][ks][i] = pv[i] * dprev[qs][ks][i];   // dP - delta
       }
     }
     pack(sv, sbf);
@@ -708,7 +710,15 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
           bf16x8 sbf[KS];
           if (t > 0) finish_ds(stage(std::integral_constant<int, ST + NS - 1>{}),
                                &xbuf[(ST + 1) & 1][kg][0], dprev, sbf);
-          products(stage(STc) + TILE, dprev);
+          // dP - delta: the accumulators start at -delta of the tile's queries
+          const float* dl_s = reinterpret_cast<const float*>(stage(STc) + 2 * TILE) + 64;
+          f32x4 nd[2];
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs) {
+            const float4 d4 = *reinterpret_cast<const float4*>(dl_s + qs * 16 + 4 * g16);
+            nd[qs] = f32x4{-d4.x, -d4.y, -d4.z, -d4.w};
+          }
+          products(stage(STc) + TILE, dprev, nd);
           if (t > 0) accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
         }
       }
@@ -777,7 +787,8 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 // The work of a query group is split over two waves on one SIMD (waves qg and qg + 4):
 //   role P (waves 0-3): S and P, written (fp32) to an LDS exchange buffer;
 //   role dQ (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
-//     been published by the step barrier, dS and dQ^T += K^T dS^T.
+//     been published by the step barrier, dS and dQ^T += K^T dS^T.  Its dP^T accumulators
+//     start at -delta of their queries (dS is then one multiply a value).
 // Only role dQ holds the dQ accumulator (96 registers a lane), so two waves fit a SIMD,
 // all eight waves have queries at 192-token blocks, and each K/V tile is loaded once per
 // block.  The K tile is read row-wise and transposed (swizzle swz16); the V tile only
@@ -929,11 +940,15 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
 
   using Acc = f32x4[2][M];
   // S^T = K Q^T (role P, rows of the K tile) or dP^T = V dO^T (role dQ, rows of V)
-  auto products = [&](const unsigned char* rows, Acc& sacc) __attribute__((always_inline)) {
+  auto products = [&](const unsigned char* rows, Acc& sacc, bool minus_row)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int m = 0; m < M; ++m) sacc[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < M; ++m) {
+        const float c = minus_row ? -rowv[m] : 0.f;
+        sacc[ks][m] = f32x4{c, c, c, c};
+      }
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
@@ -956,7 +971,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   // unselected list positions: P = 0, by a select since an empty row has lse = -inf)
   auto step_p = [&](const unsigned char* sb, float* xb, int t, Acc& sacc)
       __attribute__((always_inline)) {
-    products(sb, sacc);
+    products(sb, sacc, false);
     const bool ragged = t * KT + KT > nkeys;   // uniform
     // TOK: the launcher takes this kernel only for blocks of more than 128 tokens, so the
     // tile's keys lie at list positions li0 (offsets below the boundary) and li0 + 1: two
@@ -1012,7 +1027,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
         const float4 p4 = *reinterpret_cast<const float4*>(xb + ((ks * M + m) * 64 + lane) * 4);
         const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[ks][i] = pv[i] * (dprev[ks][m][i] - rowv[m]);
+        for (int i = 0; i < 4; ++i) sv[ks][i] = pv[i] * dprev[ks][m][i];   // dP - delta
       }
       sbf[m] = as_bf16x8(u32x4{pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]),
                                pack_bf16x2(sv[1][0], sv[1][1]), pack_bf16x2(sv[1][2], sv[1][3])});
@@ -1073,7 +1088,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
             finish_ds(&xbuf[(ST + 1) & 1][qg][0], dprev, sbf);
             accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
           }
-          products(stage(STc) + TILE, dprev);
+          products(stage(STc) + TILE, dprev, true);   // dP^T - delta
         }
       }
     };
@@ -1321,13 +1336,14 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     const unsigned char* vb = cur + TILE;
     // K and V fragments in four batches of d-steps, each read ahead of its products, and
     // the K^T reads of dQ right after.
+    // dP accumulators start at -delta of this lane's query: the products give dP - delta
     f32x16 sacc[KSUB], dpacc[KSUB];
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         sacc[kk][v] = 0.f;
-        dpacc[kk][v] = 0.f;
+        dpacc[kk][v] = -dl;
       }
     constexpr int NB = 4;   // batches of d-steps
 #pragma unroll
@@ -1378,7 +1394,7 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kk][v], c2, -lse2));
-        dpacc[kk][v] = pv * (dpacc[kk][v] - dl);
+        dpacc[kk][v] = pv * dpacc[kk][v];   // P (dP - delta)
       }
     if (t * KT + KT > nkeys) {   // ragged last tile (uniform branch): no dS past the end
 #pragma unroll
