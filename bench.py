@@ -596,7 +596,9 @@ def summarize_profile(d, workload="l3d_55k", steps=20, warmup=5):
              "`kt_kernel_stats.csv` (every launch of the run):", "",
              "| kernel | launches | avg ms | min ms | max ms | share |", "|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:22]:
-        lines.append(f"| {_short_kernel(r['Name'])} | {r['Calls']} | "
+        kname = _short_kernel(r["Name"])
+        kname = kname if len(kname) <= 90 else kname[:87] + "..."
+        lines.append(f"| {kname} | {r['Calls']} | "
                      f"{float(r['AverageNs']) / 1e6:.3f} | {float(r['MinNs']) / 1e6:.3f} | "
                      f"{float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
     lines += ["", f"Averages over the {steps} timed launches of each sparse instance (launches "
@@ -612,6 +614,18 @@ def summarize_profile(d, workload="l3d_55k", steps=20, warmup=5):
             if sel:
                 timed[k] = sum(sel) / len(sel)
                 lines.append(f"- {k}: {timed[k]:.4f} ms")
+    # bench.py's own line from the profiled run: its event-timed stage means must agree
+    try:
+        with open(os.path.join(d, "kt.log")) as f:
+            bl = next(json.loads(x) for x in f if x.startswith('{"metric"'))
+        sm = bl["stages_ms"]
+        lines += ["", f"bench.py's own HIP-event means over the same {steps} timed steps of the "
+                  "profiled run: " + ", ".join(f"{k} {v:.4f} ms" for k, v in sm.items()) +
+                  f"; {bl['ms_per_step']:.3f} ms a step, {bl['value']:.1f} TFLOP/s "
+                  "algorithmic (the profiler's own overhead included)."]
+    except (OSError, StopIteration, KeyError, ValueError):
+        pass
+    lines += ["", "Written by `python3 bench.py --summarize-profile <out>` from the run above."]
     with open(os.path.join(out_dir, f"kernel_trace_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     # HBM traffic and MFMA work per dispatch
@@ -662,7 +676,7 @@ def summarize_profile(d, workload="l3d_55k", steps=20, warmup=5):
     with open(os.path.join(out_dir, f"hbm_traffic_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     # further counter passes (sq*): every counter of every pass, per dispatch
-    passes = sorted(x for x in os.listdir(d) if x.startswith("sq"))
+    passes = sorted(x for x in os.listdir(d) if x.startswith("sq") and os.path.isdir(os.path.join(d, x)))
     if passes:
         lines = [f"# Counters of the attention kernels: 3D layer, 55,296 tokens ({workload})", "",
                  "One rocprofv3 --pmc pass per row group below, each as", "",
