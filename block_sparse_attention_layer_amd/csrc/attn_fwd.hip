@@ -418,13 +418,22 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   static_assert(NS == 4, "the step loop is unrolled over four stages");
   constexpr float kRescaleLog2 = 8.0f;
 
-  __shared__ __attribute__((aligned(1024))) unsigned char stages[NS * 2 * TILE];
+  // one __shared__ object per stage: the compiler tells direct-to-LDS loads apart from LDS
+  // reads only by object, so with one array for all stages it would make every step wait
+  // for all loads in flight (vmcnt(0)) before its first LDS read
+  __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
   auto stage = [&](auto Ic) -> unsigned char* {
     constexpr int I = decltype(Ic)::value % NS;
-    return stages + I * (2 * TILE);
+    if constexpr (I == 0) return stage0;
+    else if constexpr (I == 1) return stage1;
+    else if constexpr (I == 2) return stage2;
+    else return stage3;
   };
 
   const Geom& g = a.g;
