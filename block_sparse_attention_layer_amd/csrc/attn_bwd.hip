@@ -23,6 +23,22 @@
 
 namespace vmoba {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// The split kernels pass P between their two roles as fp16: P lies in [0, 1], where fp16
+// keeps 11 significant bits (2^-12 relative rounding) down to 2^-14 and an absolute 2^-25
+// below, against the 2^-9 of the bf16 rounding dS takes next; it halves the exchange's LDS
+// traffic against fp32.
+// two fp32 values rounded to nearest-even fp16, packed (one v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+// half e of a packed fp16 pair times x, in fp32 (one v_fma_mix_f32: the +0 addend keeps it
+// a fused operation, exact up to the one fp32 rounding)
+__device__ __forceinline__ float mul_f16(uint32_t packed, int e, float x) {
+  const f16x2 h = __builtin_bit_cast(f16x2, packed);
+  return __builtin_fmaf(float(h[e]), x, 0.0f);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(Geom g, const T* __restrict__ o,
                                                     const T* __restrict__ dout,
@@ -373,8 +389,8 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 //   permutation.
 //
 // The work of a key group is split over two waves on one SIMD (waves kg and kg + 4 of 8):
-//   role P (waves 0-3): S, P, dV^T += dO^T P; writes P (fp32, accumulator layout) to an
-//     LDS exchange buffer;
+//   role P (waves 0-3): S, P, dV^T += dO^T P; writes P (rounded to fp16, accumulator
+//     layout) to an LDS exchange buffer;
 //   role dS (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
 //     been published by the step barrier, dS and dK^T += Q^T dS.  Its dP accumulators
 //     start at -delta of their queries, so the products give dP - delta and dS is one
@@ -424,7 +440,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage3[STAGE];
-  __shared__ __attribute__((aligned(16))) float xbuf[2][NKG][XF];
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][NKG][XF / 2];   // P, fp16 pairs
   __shared__ int32_t rows_l[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
@@ -617,7 +633,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   };
   // role P, tile t in stage sb: P to the exchange buffer, dV^T += dO^T P (sacc: the
   // registers role dS keeps its dP in)
-  auto step_p = [&](const unsigned char* sb, float* xb, Acc& sacc)
+  auto step_p = [&](const unsigned char* sb, uint32_t* xb, Acc& sacc)
       __attribute__((always_inline)) {
     const f32x4 zero[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     products(sb, sacc, zero);
@@ -642,29 +658,31 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
           pv[qs][ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[qs][ks][i], c2, -lv[i]));
           if constexpr (TOK) pv[qs][ks][i] = keep[i] ? pv[qs][ks][i] : 0.f;
         }
-        *reinterpret_cast<float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4) =
-            float4{pv[qs][ks][0], pv[qs][ks][1], pv[qs][ks][2], pv[qs][ks][3]};
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      *reinterpret_cast<u32x4*>(xb + (ks * 64 + lane) * 4) =
+          u32x4{pack_f16x2(pv[0][ks][0], pv[0][ks][1]), pack_f16x2(pv[0][ks][2], pv[0][ks][3]),
+                pack_f16x2(pv[1][ks][0], pv[1][ks][1]), pack_f16x2(pv[1][ks][2], pv[1][ks][3])};
     bf16x8 pb[KS];
     pack(pv, pb);
     accumulate(sb + TILE, pb);
   };
   // role dS: dS of the previous tile (its stage sbp, its P in xb) from dprev, then the
   // dP of the current tile (stage sb) into dprev, then dK^T += Q^T dS
-  auto finish_ds = [&](const unsigned char* sbp, const float* xb, const Acc& dprev,
+  auto finish_ds = [&](const unsigned char* sbp, const uint32_t* xb, const Acc& dprev,
                        bf16x8 (&sbf)[KS]) __attribute__((always_inline)) {
     (void)sbp;
     float sv[2][KS][4];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 p4 = *reinterpret_cast<const u32x4*>(xb + (ks * 64 + lane) * 4);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float4 p4 = *reinterpret_cast<const float4*>(xb + ((qs * KS + ks) * 64 + lane) * 4);
-        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[qs][ks][i] = pv[i] * dprev[qs][ks][i];   // dP - delta
-      }
+        for (int i = 0; i < 4; ++i)   // P (dP - delta)
+          sv[qs][ks][i] = mul_f16(p4[2 * qs + (i >> 1)], i & 1, dprev[qs][ks][i]);
     }
     pack(sv, sbf);
   };
@@ -745,7 +763,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   if (wave_busy && !role_p && ntiles > 0) {
     const int last = ntiles - 1;
     bf16x8 sbf[KS];
-    const float* xb = &xbuf[last & 1][kg][0];
+    const uint32_t* xb = &xbuf[last & 1][kg][0];
     switch (last & 3) {
       case 0: finish_ds(stage0, xb, dprev, sbf); accumulate(stage0, sbf); break;
       case 1: finish_ds(stage1, xb, dprev, sbf); accumulate(stage1, sbf); break;
@@ -785,7 +803,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 //   to the accumulator layout (as P in the forward): the B operand of dQ^T += K^T dS^T,
 //   whose A operand K^T comes from two transposing reads of the K tile.
 // The work of a query group is split over two waves on one SIMD (waves qg and qg + 4):
-//   role P (waves 0-3): S and P, written (fp32) to an LDS exchange buffer;
+//   role P (waves 0-3): S and P, written (rounded to fp16) to an LDS exchange buffer;
 //   role dQ (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
 //     been published by the step barrier, dS and dQ^T += K^T dS^T.  Its dP^T accumulators
 //     start at -delta of their queries (dS is then one multiply a value).
@@ -817,7 +835,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
-  __shared__ __attribute__((aligned(16))) float xbuf[2][NQG][XF];
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][NQG][XF / 2];   // P, fp16 pairs
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
@@ -969,7 +987,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   }
   // role P, tile t in stage sb: P to the exchange buffer (keys past the end, and with TOK
   // unselected list positions: P = 0, by a select since an empty row has lse = -inf)
-  auto step_p = [&](const unsigned char* sb, float* xb, int t, Acc& sacc)
+  auto step_p = [&](const unsigned char* sb, uint32_t* xb, int t, Acc& sacc)
       __attribute__((always_inline)) {
     products(sb, sacc, false);
     const bool ragged = t * KT + KT > nkeys;   // uniform
@@ -1010,25 +1028,23 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
           }
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        *reinterpret_cast<float4*>(xb + ((ks * M + m) * 64 + lane) * 4) =
-            float4{pv[ks][m][0], pv[ks][m][1], pv[ks][m][2], pv[ks][m][3]};
+    for (int m = 0; m < M; ++m)
+      *reinterpret_cast<u32x4*>(xb + (m * 64 + lane) * 4) =
+          u32x4{pack_f16x2(pv[0][m][0], pv[0][m][1]), pack_f16x2(pv[0][m][2], pv[0][m][3]),
+                pack_f16x2(pv[1][m][0], pv[1][m][1]), pack_f16x2(pv[1][m][2], pv[1][m][3])};
   };
   // role dQ: dS^T of the previous tile (P in xb, dP in dprev), packed as B operands
-  auto finish_ds = [&](const float* xb, const Acc& dprev, bf16x8 (&sbf)[M])
+  auto finish_ds = [&](const uint32_t* xb, const Acc& dprev, bf16x8 (&sbf)[M])
       __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float sv[2][4];
+      const u32x4 p4 = *reinterpret_cast<const u32x4*>(xb + (m * 64 + lane) * 4);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const float4 p4 = *reinterpret_cast<const float4*>(xb + ((ks * M + m) * 64 + lane) * 4);
-        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[ks][i] = pv[i] * dprev[ks][m][i];   // dP - delta
-      }
+        for (int i = 0; i < 4; ++i)   // P (dP - delta)
+          sv[ks][i] = mul_f16(p4[2 * ks + (i >> 1)], i & 1, dprev[ks][m][i]);
       sbf[m] = as_bf16x8(u32x4{pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]),
                                pack_bf16x2(sv[1][0], sv[1][1]), pack_bf16x2(sv[1][2], sv[1][3])});
     }
