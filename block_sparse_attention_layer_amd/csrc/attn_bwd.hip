@@ -417,7 +417,7 @@ __device__ __forceinline__ int swz16(int r) { return 2 * (r & 7); }
 // TOK: token-granular selection; role P keeps P only where the query token's key-block
 // mask has this block's bit (dS then vanishes with it).  Wave 2 loads the tile's mask
 // words into its slot instead of an LSE copy.
-template <bool DENSE, bool TAB, typename GT, bool TOK = false>
+template <bool DENSE, bool TAB, typename GT, bool TOK = false, bool ALN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 8, NT = 512, NKG = 4;
@@ -499,7 +499,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
     __syncthreads();
     nq = kept * g.S;
   }
-  const int ntiles = (nq + QT - 1) / QT;
+  const int ntiles = __builtin_amdgcn_readfirstlane((nq + QT - 1) / QT);
 
   // this wave's keys: K (role P) or V (role dS) columns, the B operands, in registers
   const int klim = DENSE ? g.L : g.S;
@@ -550,7 +550,24 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
     }
   };
   // element offset of this lane's Q/dO row of tile t, and the token of its LSE/delta
+  // ALN (blocks a multiple of the tile): tile t lies in one list entry, at rows aln_rr.. of
+  // it; the entry and row advance by one tile a call (calls come in tile order) and stop
+  // at the last tile, which the tiles past the end repeat
+  int aln_pb = 0, aln_rr = 0;
   auto tile_offsets = [&](int t, int32_t& o, int32_t& xl) {
+    if constexpr (ALN) {
+      const int32_t rb = rows_l[aln_pb];
+      o = gbase + (rb + offtab[aln_rr + lrow]) * hstride;
+      xl = rb + offtab[aln_rr + (lane & 31)];
+      if (t + 1 < ntiles) {
+        aln_rr += QT;
+        if (aln_rr == g.S) {
+          aln_rr = 0;
+          ++aln_pb;
+        }
+      }
+      return;
+    }
     o = gbase + qtoken(min(t * QT + lrow, plast)) * hstride;
     xl = qtoken(min(t * QT + (lane & 31), plast));
   };
@@ -815,7 +832,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 // TOK: token-granular selection; role P keeps P only at the list positions its query
 // selected (the query's row of the list-position mask, two words cached per sub-tile and
 // refetched when a tile moves into another 32-position window).
-template <bool DENSE, bool TAB, typename GT, bool TOK = false>
+template <bool DENSE, bool TAB, typename GT, bool TOK = false, bool ALN = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 8, NT = 512, NQG = 4;
@@ -886,14 +903,17 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
     list_range(g, a.row_ptr, grp, iblk, &start, &len);
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
-    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
-    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: loads of an empty stream
+    // ALN: the tables hold element offsets (token times the row stride, plus the head's
+    // base in cols), so a tile's row offset is one addition
+    const int32_t hs = ALN ? g.Hh * D : 1, gb = ALN ? row_offset(g, grp, 0) : 0;
+    for (int i = tid; i < kept; i += NT) cols[i] = gb + block_base(g, uint32_t(cols[i])) * hs;
+    if (kept == 0 && tid == 0) cols[0] = gb;   // token 0: loads of an empty stream
     if constexpr (TAB)
-      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r)) * hs;
     __syncthreads();
     nkeys = kept * g.S;
   }
-  const int ntiles = (nkeys + KT - 1) / KT;
+  const int ntiles = __builtin_amdgcn_readfirstlane((nkeys + KT - 1) / KT);
 
   // this lane's query in each sub-tile; Q (role P) or dO (role dQ) fragments in registers
   const int qlim = DENSE ? g.L : g.S;
@@ -924,7 +944,20 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   const int plast = max(nkeys - 1, 0);   // positions past the end repeat the last key
   const int lrow = w * (KT / NW) + g16;
   const int chunk = (i16 ^ swz16(lrow)) * 8;
+  // ALN (blocks a multiple of the tile): as in the dK/dV kernel
+  int aln_pb = 0, aln_rr = 0;
   auto tile_offsets = [&](int t) -> int32_t {
+    if constexpr (ALN) {
+      const int32_t o = cols[aln_pb] + offtab[aln_rr + lrow];
+      if (t + 1 < ntiles) {
+        aln_rr += KT;
+        if (aln_rr == g.S) {
+          aln_rr = 0;
+          ++aln_pb;
+        }
+      }
+      return o;
+    }
     const int p = min(t * KT + lrow, plast);
     int32_t x = p;
     if constexpr (!DENSE) {
@@ -1703,7 +1736,9 @@ static void launch_dkdv_split_bf16(AttnParams a, hipStream_t s) {
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 191) / 192;
   const int grid = launch_grid<DENSE>(a, rows);
-  if (!DENSE && g.S <= kOffsetTable)
+  if (!DENSE && g.S <= kOffsetTable && g.S % 32 == 0)
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK, !DENSE><<<grid, 512, 0, s>>>(a);
+  else if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK><<<grid, 512, 0, s>>>(a);
   else
     attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT, TOK><<<grid, 512, 0, s>>>(a);
@@ -1738,7 +1773,9 @@ static void launch_dq_split_bf16(AttnParams a, hipStream_t s) {
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + 191) / 192;
   const int grid = launch_grid<DENSE>(a, rows);
-  if (!DENSE && g.S <= kOffsetTable)
+  if (!DENSE && g.S <= kOffsetTable && g.S % 32 == 0)
+    attn_bwd_dq_split_bf16_kernel<DENSE, !DENSE, GT, TOK, !DENSE><<<grid, 512, 0, s>>>(a);
+  else if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dq_split_bf16_kernel<DENSE, !DENSE, GT, TOK><<<grid, 512, 0, s>>>(a);
   else
     attn_bwd_dq_split_bf16_kernel<DENSE, false, GT, TOK><<<grid, 512, 0, s>>>(a);

@@ -405,7 +405,7 @@ void attn_fwd_bf16_kernel(AttnParams a) {
 // sits at position c ^ (r & 15), so the 16 rows of a K fragment read hit 16 different bank
 // groups; V chunk c of row r sits at c ^ 2 (r & 7), so the 8 rows x 32 bytes of a
 // half-wave's transposing read cover all 64 banks.
-template <int M, int NS, bool DENSE, bool TAB>
+template <int M, int NS, bool DENSE, bool TAB, bool ALN = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd16_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 4, NT = 256;
@@ -472,14 +472,17 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
     list_range(g, a.row_ptr, grp, iblk, &start, &len);
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
-    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
-    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: loads of an empty stream
+    // ALN: the tables hold element offsets (token times the row stride, plus the head's
+    // base in cols), so a tile's row offsets are one addition
+    const int32_t hs = ALN ? g.Hh * D : 1, gb = ALN ? row_offset(g, grp, 0) : 0;
+    for (int i = tid; i < kept; i += NT) cols[i] = gb + block_base(g, uint32_t(cols[i])) * hs;
+    if (kept == 0 && tid == 0) cols[0] = gb;   // token 0: loads of an empty stream
     if constexpr (TAB)
-      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r)) * hs;
     __syncthreads();
     nkeys = kept * g.S;
   }
-  const int ntiles = (nkeys + KT - 1) / KT;
+  const int ntiles = __builtin_amdgcn_readfirstlane((nkeys + KT - 1) / KT);
 
   // this lane's query in each sub-tile; Q fragments (B operands) in registers
   const int qlim = DENSE ? g.L : g.S;
@@ -522,7 +525,25 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
     kchunk[i] = (i16 ^ (r & 15)) * 8;
     vchunk[i] = (i16 ^ (2 * (r & 7))) * 8;
   }
+  // ALN (blocks a multiple of the tile): tile t lies in one list entry, at rows
+  // aln_rr.. of it; the entry and row advance by one tile a call (calls come in tile
+  // order) and stop at the last tile, which the tiles past the end repeat
+  int aln_pb = 0, aln_rr = 0;
+  const int aln_row = w * (KT / NW) + g16;   // this lane's row of the tile, first load
   auto tile_offsets = [&](int t, int32_t (&o)[LPW]) {
+    if constexpr (ALN) {
+      const int32_t cb = cols[aln_pb];
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) o[i] = cb + offtab[aln_rr + aln_row + i * 4];
+      if (t + 1 < ntiles) {
+        aln_rr += KT;
+        if (aln_rr == g.S) {
+          aln_rr = 0;
+          ++aln_pb;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int p = min(t * KT + w * (KT / NW) + i * 4 + g16, plast);
@@ -836,7 +857,9 @@ static void launch_fwd16_bf16(AttnParams& a, hipStream_t s) {
   a.tiles = (qlim + 64 * M - 1) / (64 * M);
   const int rows = DENSE ? 1 : g.Nb;
   const int grid = launch_grid<DENSE>(a, rows);
-  if (!DENSE && g.S <= kOffsetTable)
+  if (!DENSE && g.S <= kOffsetTable && g.S % 32 == 0)
+    attn_fwd16_bf16_kernel<M, 4, DENSE, !DENSE, !DENSE><<<grid, 256, 0, s>>>(a);
+  else if (!DENSE && g.S <= kOffsetTable)
     attn_fwd16_bf16_kernel<M, 4, DENSE, !DENSE><<<grid, 256, 0, s>>>(a);
   else
     attn_fwd16_bf16_kernel<M, 4, DENSE, false><<<grid, 256, 0, s>>>(a);
