@@ -1198,7 +1198,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
 // loads on the same counter), the loads of tile t+1 are in flight during tile t and the
 // step ends waiting for all of them.
 template <int D, int NW, int KSUB, bool DENSE, bool TAB, typename GT, bool TOK = false,
-          int NS = 2>
+          int NS = 2, bool ALN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_bf16_kernel(AttnParams a) {
   constexpr int NT = NW * 64;
@@ -1262,14 +1262,17 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
     list_range(g, a.row_ptr, grp, iblk, &start, &len);
     const int kept = compact_list<NT>(a.col_idx + size_t(grp) * g.Nb * g.Nb + start, len,
                                       g.Nb, cols, scratch);
-    for (int i = tid; i < kept; i += NT) cols[i] = block_base(g, uint32_t(cols[i]));
-    if (kept == 0 && tid == 0) cols[0] = 0;   // token 0: address of an empty stream
+    // ALN: the tables hold element offsets (token times the row stride, plus the head's
+    // base in cols), so a tile's row offsets are one addition
+    const int32_t hs = ALN ? g.Hh * D : 1, gb = ALN ? row_offset(g, grp, 0) : 0;
+    for (int i = tid; i < kept; i += NT) cols[i] = gb + block_base(g, uint32_t(cols[i])) * hs;
+    if (kept == 0 && tid == 0) cols[0] = gb;   // token 0: address of an empty stream
     if constexpr (TAB)
-      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r));
+      for (int r = tid; r < g.S; r += NT) offtab[r] = block_offset(g, uint32_t(r)) * hs;
     __syncthreads();
     nkeys = kept * g.S;
   }
-  const int ntiles = (nkeys + KT - 1) / KT;
+  const int ntiles = __builtin_amdgcn_readfirstlane((nkeys + KT - 1) / KT);
 
   const int qlim = DENSE ? g.L : g.S;
   const int rq = qt * QT + w * 32 + l32;
@@ -1303,7 +1306,27 @@ void attn_bwd_dq_bf16_kernel(AttnParams a) {
   const int32_t gbase = row_offset(g, grp, 0);
   const int plast = max(nkeys - 1, 0);   // positions past the end repeat the last key
   // element offsets of this lane's K/V rows of tile t (addresses first, loads back to back)
+  // ALN (blocks a multiple of the tile): tile t lies in one list entry, at rows aln_rr.. of
+  // it; the entry and row advance by one tile a call (calls come in tile order) and stop
+  // at the last tile, which the tiles past the end repeat
+  int aln_pb = 0, aln_rr = 0;
   auto tile_offsets = [&](int t, int32_t (&o)[LPW]) {
+    if constexpr (ALN) {
+      const int32_t cb = cols[aln_pb];
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = lrow0 + i * RPI;
+        o[i] = cb + offtab[aln_rr + r] + (lcp ^ swz<D>(r)) * 8;
+      }
+      if (t + 1 < ntiles) {
+        aln_rr += KT;
+        if (aln_rr == g.S) {
+          aln_rr = 0;
+          ++aln_pb;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = lrow0 + i * RPI;
@@ -1803,7 +1826,10 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   a.tiles = (lim + 127) / 128;
   const int grid = launch_grid<DENSE>(a, rows);
   constexpr int NS = TOK ? 2 : 4;
-  if (!DENSE && g.S <= kOffsetTable)
+  if (!DENSE && g.S <= kOffsetTable && g.S % (KSUB * 32) == 0)
+    attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK, NS, !DENSE>
+        <<<grid, 256, 0, s>>>(a);
+  else if (!DENSE && g.S <= kOffsetTable)
     attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, !DENSE, GT, TOK, NS><<<grid, 256, 0, s>>>(a);
   else
     attn_bwd_dq_bf16_kernel<D, 4, KSUB, DENSE, false, GT, TOK, NS><<<grid, 256, 0, s>>>(a);
