@@ -507,11 +507,15 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) oacc[m][ds] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[M], l_run[M];
+  // running max, and derived from it (updated only when it moves): the rescale
+  // threshold m + thr and the exponent offset m * c2
+  float m_run[M], l_run[M], m_thr[M], m_off[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     m_run[m] = -INFINITY;
     l_run[m] = 0.f;
+    m_thr[m] = -INFINITY;
+    m_off[m] = -INFINITY;
   }
 
   // loader: one instruction moves 4 rows; lane L fills row L/16 at chunk position L % 16
@@ -620,7 +624,7 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
       const u32x2 hi = lds_read_tr16(sm + 16 * ROWB + voff[ds]);
       va[ds] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    if (t * KT + KT > nkeys) {   // ragged last tile: keys past the end score -inf
+    if (!ALN && t * KT + KT > nkeys) {   // ragged last tile: keys past the end score -inf
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -651,26 +655,28 @@ void attn_fwd16_bf16_kernel(AttnParams a) {
       v = max3f(v, sacc[1][m][1], sacc[1][m][2]);
       v = __builtin_elementwise_maximum(v, sacc[1][m][3]);
       mx[m] = DENSE ? row_max(v) : v;
-      any |= mx[m] > m_run[m] + thr;
+      any |= mx[m] > m_thr[m];
     }
     // lazy rescale (wave-uniform): every sub-tile on the first tile, rarely afterwards
     if (__ballot(any)) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float v = DENSE ? mx[m] : row_max(mx[m]);
-        const float m_new = v > m_run[m] + thr ? v : m_run[m];
+        const float m_new = v > m_thr[m] ? v : m_run[m];
         const float alpha = __builtin_amdgcn_exp2f((m_run[m] - m_new) * c2);
         l_run[m] *= alpha;
 #pragma unroll
         for (int ds = 0; ds < D / 16; ++ds) oacc[m][ds] *= alpha;
         m_run[m] = m_new;
+        m_thr[m] = m_new + thr;
+        m_off[m] = m_new * c2;
       }
     }
     // P = exp2(S c2 - m c2), packed in the permuted k order
     u32x4 pw[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float moff = m_run[m] * c2;
+      const float moff = m_off[m];
       float p[2][4];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
