@@ -684,16 +684,23 @@ def summarize_profile(d, workload="l3d_55k", steps=20, warmup=5):
                  "", "Values are means per dispatch of the sparse instances, summed over the "
                  "chip as rocprofv3 reports them (SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_* are in "
                  "quad-cycles; GRBM_GUI_ACTIVE is summed over the 8 XCDs).", ""]
-        kernels = ["attn_fwd16_bf16_kernel<3, 4, false, true>",
-                   "attn_bwd_dkdv_split_bf16_kernel<false, true, bf16, false>",
-                   "attn_bwd_dq_split_bf16_kernel<false, true, bf16, false>"]
-        lines.append("| pass | counter | " + " | ".join(k.split("<")[0] for k in kernels) + " |")
-        lines.append("|---|---|" + "---|" * len(kernels))
+        bases = ["attn_fwd16_bf16_kernel", "attn_bwd_dkdv_split_bf16_kernel",
+                 "attn_bwd_dq_split_bf16_kernel"]
+        all_vals = {}
         for ps in passes:
             vals = {}
             for r in _csv_rows(_find(os.path.join(d, ps), "counter_collection.csv")):
                 k = _short_kernel(r["Kernel_Name"])
                 vals.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+            all_vals[ps] = vals
+        # the sparse instance of each kernel (the dense ones carry "true, false")
+        seen = {k for vals in all_vals.values() for (_, k) in vals}
+        kernels = [next((k for k in sorted(seen) if k.split("<")[0] == b and "true, false" not in k),
+                        b) for b in bases]
+        lines.append("| pass | counter | " + " | ".join(k.split("<")[0] for k in kernels) + " |")
+        lines.append("|---|---|" + "---|" * len(kernels))
+        for ps in passes:
+            vals = all_vals[ps]
             for ctr in sorted({c for c, _ in vals}):
                 cells = []
                 for k in kernels:
