@@ -114,10 +114,8 @@ int vmoba_sparse_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
   const Geom g = make_geom(p);
   float* delta = static_cast<float*>(ws);
   if ((st = launch_bwd_delta(g, o, dout, delta, stream))) return st;
-  if ((st = launch_bwd_dkdv(g, false, q, k, v, lse, delta, dout, col_ptr, row_idx, dk, dv,
-                            stream)))
-    return st;
-  return launch_bwd_dq(g, false, q, k, v, lse, delta, dout, row_ptr, col_idx, dq, stream);
+  return launch_bwd_dkdv_dq(g, q, k, v, lse, delta, dout, row_ptr, col_idx, col_ptr, row_idx,
+                            dq, dk, dv, stream);
 }
 
 int vmoba_sparse_attn_bwd_delta(const vmoba_problem* p, const void* o, const void* dout,

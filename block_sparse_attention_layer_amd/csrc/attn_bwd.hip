@@ -17,6 +17,7 @@
 //    S^T = K Q^T and dP^T = V dO^T, and K once more transposed for dQ^T += K^T dS^T.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1926,6 +1927,73 @@ int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const
   if (g.dtype == VMOBA_BF16) VMOBA_DISPATCH_BF16(launch_dq_bf16, a, s, dense);
   else VMOBA_DISPATCH_F32(launch_dq_f32, a, s, dense);
   return launch_status();
+}
+
+// dK/dV and dQ side by side: dQ on a second stream of the device, forked from `stream`
+// after what is already queued there (delta) and joined back into it.  The two kernels
+// read the same inputs and write disjoint outputs; each fills one workgroup a CU, so
+// running them together lets the second fill the CUs the first leaves idle at its tail.
+// The second stream is made once per device (default priority) and kept; the fork and
+// join events are made and released per call.  Without a second stream the two run one
+// after the other on `stream`.
+namespace {
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxSideDevices] = {};
+
+hipStream_t side_stream(int dev) {
+  if (dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (!g_side[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    hipStream_t s = nullptr;
+    const hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return nullptr;
+    g_side[dev] = s;
+  }
+  return g_side[dev];
+}
+}  // namespace
+
+int launch_bwd_dkdv_dq(const Geom& g, const void* q, const void* k, const void* v,
+                       const float* lse, const float* delta, const void* dout,
+                       const int32_t* row_ptr, const int32_t* col_idx,
+                       const int32_t* col_ptr, const int32_t* row_idx, void* dq, void* dk,
+                       void* dv, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  const bool have_dev =
+      s ? hipStreamGetDevice(s, &dev) == hipSuccess : hipGetDevice(&dev) == hipSuccess;
+  hipStream_t side = have_dev ? side_stream(dev) : nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (side && (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess)) {
+    if (fork) (void)hipEventDestroy(fork);
+    side = nullptr;
+  }
+  if (!side) {
+    int st = launch_bwd_dkdv(g, false, q, k, v, lse, delta, dout, col_ptr, row_idx, dk, dv,
+                             stream);
+    if (st) return st;
+    return launch_bwd_dq(g, false, q, k, v, lse, delta, dout, row_ptr, col_idx, dq, stream);
+  }
+  int st = VMOBA_OK;
+  if (hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
+    st = VMOBA_ERR_HIP;
+  if (!st)
+    st = launch_bwd_dkdv(g, false, q, k, v, lse, delta, dout, col_ptr, row_idx, dk, dv,
+                         stream);
+  if (!st) st = launch_bwd_dq(g, false, q, k, v, lse, delta, dout, row_ptr, col_idx, dq, side);
+  // the join is recorded even after a failed launch, so that `stream` never runs ahead of
+  // work queued on the second stream
+  if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess)
+    st = st ? st : VMOBA_ERR_HIP;
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  return st;
 }
 
 // Token-granular selection: dK/dV over the column lists under the key-block mask, dQ over

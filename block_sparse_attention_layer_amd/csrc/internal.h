@@ -73,4 +73,12 @@ int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const
                   const float* lse, const float* delta, const void* dout,
                   const int32_t* row_ptr, const int32_t* col_idx, void* dq, void* stream);
 
+// The sparse dK/dV and dQ of one backward, dQ on a second stream of the device (forked
+// from and joined back into `stream`), or both on `stream` when no second stream is had.
+int launch_bwd_dkdv_dq(const Geom& g, const void* q, const void* k, const void* v,
+                       const float* lse, const float* delta, const void* dout,
+                       const int32_t* row_ptr, const int32_t* col_idx,
+                       const int32_t* col_ptr, const int32_t* row_idx, void* dq, void* dk,
+                       void* dv, void* stream);
+
 }  // namespace vmoba

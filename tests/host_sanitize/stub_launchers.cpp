@@ -102,4 +102,12 @@ int launch_bwd_dq(const Geom&, bool dense, const void* q, const void* k, const v
   return ++g_launches, VMOBA_OK;
 }
 
+int launch_bwd_dkdv_dq(const Geom&, const void* q, const void* k, const void* v,
+                       const float* lse, const float* delta, const void* dout,
+                       const int32_t* rp, const int32_t* ci, const int32_t* cp,
+                       const int32_t* ri, void* dq, void* dk, void* dv, void*) {
+  NEED(q && k && v && lse && delta && dout && rp && ci && cp && ri && dq && dk && dv);
+  return g_launches += 2, VMOBA_OK;
+}
+
 }  // namespace vmoba
