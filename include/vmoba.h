@@ -172,7 +172,10 @@ int vmoba_sparse_attn_fwd(const vmoba_problem* p, const void* q, const void* k,
  * pairs as the CSR.  o, lse: outputs of the forward.  dq, dk, dv: [B][L][Hh][d]
  * grad_dtype, written in full (rows of key tokens no query attends to get zeros).  With
  * grad_dtype bf16 each gradient is the round-to-nearest-even of its fp32 value.
- * ws: vmoba_workspace_size(VMOBA_OP_SPARSE_BWD) bytes. */
+ * ws: vmoba_workspace_size(VMOBA_OP_SPARSE_BWD) bytes.  The dQ pass runs on a second
+ * stream of the device, made on first use and kept, forked from `stream` after delta and
+ * joined back before the call returns: work queued on `stream` afterwards sees all three
+ * gradients, and the call may be captured in a graph from `stream`. */
 int vmoba_sparse_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
                           const void* v, const void* o, const float* lse,
                           const void* dout, const int32_t* row_ptr,
