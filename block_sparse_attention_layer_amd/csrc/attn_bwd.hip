@@ -435,7 +435,7 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   // per stage: Q tile, dO tile, then eight 64-float slots: LSE (even waves), delta (odd);
   // every wave loads one slot so that all waves count the same loads per tile
   constexpr int STAGE = 2 * TILE + NW * 64 * 4;
-  constexpr int XF = 2 * KS * 4 * 64;        // floats of P one key group passes a tile
+  constexpr int XF = 2 * KS * 4 * 64;        // values of P one key group passes a tile
 
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
@@ -847,7 +847,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   static_assert(LPW == 1, "one row group per wave");
   constexpr int NS = 4;                      // pipeline stages
   constexpr int PER_TILE = 2 * LPW;          // loads per wave per tile
-  constexpr int XF = 2 * M * 4 * 64;         // floats of P one query group passes a tile
+  constexpr int XF = 2 * M * 4 * 64;         // values of P one query group passes a tile
 
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
