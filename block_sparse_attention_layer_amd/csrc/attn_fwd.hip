@@ -905,9 +905,14 @@ int launch_attn_fwd(const Geom& g, bool dense, const void* q, const void* k,
       if (m3) {
         if (dense) launch_fwd16_bf16<3, true>(a, s);
         else launch_fwd16_bf16<3, false>(a, s);
+      } else if (dense) {
+        launch_fwd_bf16<128, 4, 1, 4, true>(a, s);
+      } else if (qlim > 128 && qlim <= 256) {
+        // blocks of 193-256 tokens: eight waves, one workgroup a block, so the block's
+        // key list is streamed once instead of by two workgroups (216-token blocks: 3-5 %)
+        launch_fwd_bf16<128, 8, 1, 4, false>(a, s);
       } else {
-        if (dense) launch_fwd_bf16<128, 4, 1, 4, true>(a, s);
-        else launch_fwd_bf16<128, 4, 1, 4, false>(a, s);
+        launch_fwd_bf16<128, 4, 1, 4, false>(a, s);
       }
     } else {
       if (dense) launch_fwd_bf16<64, 4, 2, 4, true>(a, s);

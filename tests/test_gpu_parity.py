@@ -29,6 +29,8 @@ CASES = [
     ("tiny_bf16", "tiny", {}, LayerSpec(2, (2, 4, 4)), 0.25, "bf16", 64, 1),
     ("small3d_192", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.25, "bf16", 128, 1),
     ("small3d_216", "cycle_76k", dict(T=6, H=18, W=16), LayerSpec(2, (3, 9, 8)), 0.25, "bf16", 128, 1),
+    # 256-token blocks: every wave of the eight-wave 32-query forward holds queries
+    ("small3d_256", "l3d_55k", dict(T=8, H=16, W=16), LayerSpec(2, (4, 8, 8)), 0.4, "bf16", 128, 1),
     ("small2d_168", "l2d_32k", dict(T=7, H=18, W=12), LayerSpec(1, (7, 6, 4)), 0.25, "bf16", 128, 1),
     ("small1d_120", "l1d_32k", dict(T=6, H=10, W=12), LayerSpec(0, (1, 10, 12)), 0.25, "bf16", 128, 1),
     ("small3d_d64_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.5, "bf16", 64, 2),
