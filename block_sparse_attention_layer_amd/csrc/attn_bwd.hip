@@ -17,7 +17,6 @@
 //    S^T = K Q^T and dP^T = V dO^T, and K once more transposed for dQ^T += K^T dS^T.
 #include <math.h>
 
-#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1933,18 +1932,19 @@ int launch_bwd_dq(const Geom& g, bool dense, const void* q, const void* k, const
 // after what is already queued there (delta) and joined back into it.  The two kernels
 // read the same inputs and write disjoint outputs; each fills one workgroup a CU, so
 // running them together lets the second fill the CUs the first leaves idle at its tail.
-// The second stream is made once per device (default priority) and kept; the fork and
-// join events are made and released per call.  Without a second stream the two run one
-// after the other on `stream`.
+// The second stream is made once per host thread and device (default priority) and kept
+// until the process ends: a stream shared between threads would take one thread's work
+// into another thread's graph capture while that capture runs.  It is not made while
+// `stream` is being captured.  The fork and join events are made and released per call.
+// Without a second stream the two run one after the other on `stream`.
 namespace {
 constexpr int kMaxSideDevices = 64;
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxSideDevices] = {};
+thread_local hipStream_t t_side[kMaxSideDevices] = {};
 
-hipStream_t side_stream(int dev) {
+// create: whether a missing stream may be made now (not while `stream` is being captured)
+hipStream_t side_stream(int dev, bool create) {
   if (dev < 0 || dev >= kMaxSideDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  if (!g_side[dev]) {
+  if (!t_side[dev] && create) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return nullptr;
     if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
@@ -1952,9 +1952,9 @@ hipStream_t side_stream(int dev) {
     const hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
     if (cur != dev) (void)hipSetDevice(cur);
     if (e != hipSuccess) return nullptr;
-    g_side[dev] = s;
+    t_side[dev] = s;
   }
-  return g_side[dev];
+  return t_side[dev];
 }
 }  // namespace
 
@@ -1967,7 +1967,12 @@ int launch_bwd_dkdv_dq(const Geom& g, const void* q, const void* k, const void* 
   int dev = -1;
   const bool have_dev =
       s ? hipStreamGetDevice(s, &dev) == hipSuccess : hipGetDevice(&dev) == hipSuccess;
-  hipStream_t side = have_dev ? side_stream(dev) : nullptr;
+  // (the null stream is never captured; asking about it could fail while another stream
+  // is captured, and leave that error for the launch checks below)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const bool capturing =
+      s && (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone);
+  hipStream_t side = have_dev ? side_stream(dev, !capturing) : nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   if (side && (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
                hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess)) {

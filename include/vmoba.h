@@ -21,8 +21,11 @@
  *   col_ptr, row_idx, head_stats, norm_scores and ws are DEVICE pointers; `p` and `bytes`
  *   / `nb` out-parameters are HOST pointers.  `stream` is a hipStream_t (NULL = the null
  *   stream).  Every GPU call only enqueues work on `stream` and returns; no call
- *   allocates, frees or synchronises, and the library keeps no state, so calls from
- *   several host threads are safe.  The caller owns every buffer.
+ *   allocates or frees device memory or synchronises, and calls from several host
+ *   threads are safe.  The library keeps two kinds of state: vmoba_sparse_attn_bwd's
+ *   second stream (one per host thread and device, kept until the process ends) and
+ *   vmoba_sparse_attn_bwd_noalloc's fixed scratch array (one per device).  The caller
+ *   owns every buffer.
  * - Token layout: Q, K, V, O, dO, dQ, dK, dV are contiguous [B][L][Hh][d] with
  *   L = T*H*W and token (t, h, w) at index (t*H + h)*W + w (frame-first flattening).
  *   Element type is `dtype` (bf16 or fp32) for Q, K, V, O, dO and `grad_dtype` for
@@ -173,9 +176,12 @@ int vmoba_sparse_attn_fwd(const vmoba_problem* p, const void* q, const void* k,
  * grad_dtype, written in full (rows of key tokens no query attends to get zeros).  With
  * grad_dtype bf16 each gradient is the round-to-nearest-even of its fp32 value.
  * ws: vmoba_workspace_size(VMOBA_OP_SPARSE_BWD) bytes.  The dQ pass runs on a second
- * stream of the device, made on first use and kept, forked from `stream` after delta and
- * joined back before the call returns: work queued on `stream` afterwards sees all three
- * gradients, and the call may be captured in a graph from `stream`. */
+ * stream of the device (one per calling host thread, made on its first call there and
+ * kept), forked from `stream` after delta and joined back before the call returns: work
+ * queued on `stream` afterwards sees all three gradients, and the call may be captured
+ * in a graph from `stream`.  If that stream cannot be made, or this thread's first call
+ * comes while `stream` is being captured, the passes run one after the other on
+ * `stream`. */
 int vmoba_sparse_attn_bwd(const vmoba_problem* p, const void* q, const void* k,
                           const void* v, const void* o, const float* lse,
                           const void* dout, const int32_t* row_ptr,

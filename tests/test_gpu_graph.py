@@ -1,7 +1,8 @@
 """The whole step (pool, select, forward, backward) captured in one HIP graph.
 
-The library allocates nothing, issues no memset (its selection clears its tables with a
-fill kernel) and keeps no state, so a caller can capture a step and replay it.  Every
+The library allocates nothing and issues no memset (its selection clears its tables with
+a fill kernel), and the backward's second stream is made on an eager call before the
+capture, so a caller can capture a step and replay it.  Every
 kernel is deterministic (the selection's atomics add integers), so each replay must
 reproduce the eager step bit for bit.  Replays alternate with eager steps on the same
 buffers' neighbours, and every replay is checked.
