@@ -177,9 +177,8 @@ def dkdv_kernel_name(klim, head_dim, bf16):
 def dq_kernel_name(qlim, head_dim, bf16):
     """The dQ kernel the library launches: 192 queries a workgroup in query groups of 48,
     each split over two waves, at d = 128 when 192-query tiles pad no more than 128-query
-    ones and those would leave more than an eighth of their query slots empty."""
-    p128 = -(-qlim // 128) * 128
-    if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= p128 and (p128 - qlim) * 8 > p128:
+    ones."""
+    if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= -(-qlim // 128) * 128:
         return "attn_bwd_dq_split_bf16_kernel"
     return "attn_bwd_dq_bf16_kernel"
 

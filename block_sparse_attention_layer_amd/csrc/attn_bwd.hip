@@ -820,15 +820,19 @@ void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
 //   to the accumulator layout (as P in the forward): the B operand of dQ^T += K^T dS^T,
 //   whose A operand K^T comes from two transposing reads of the K tile.
 // The work of a query group is split over two waves on one SIMD (waves qg and qg + 4):
-//   role P (waves 0-3): S and P, written (rounded to fp16) to an LDS exchange buffer;
-//   role dQ (waves 4-7): dP of tile t, and one step later, once role P's P of tile t has
-//     been published by the step barrier, dS and dQ^T += K^T dS^T.  Its dP^T accumulators
-//     start at -delta of their queries (dS is then one multiply a value).
-// Only role dQ holds the dQ accumulator (96 registers a lane), so two waves fit a SIMD,
-// all eight waves have queries at 192-token blocks, and each K/V tile is loaded once per
-// block.  The K tile is read row-wise and transposed (swizzle swz16); the V tile only
-// row-wise (same swizzle).  Stages as in the split dK/dV kernel: tile t is read at steps
-// t and t+1, step t refills the stage of tile t-2 with tile t+2.
+//   role P (waves 0-3): S and dP of tile t (its dP^T accumulators start at -delta of their
+//     queries), P, and dS = P (dP - delta) from the fp32 P, packed in bf16 as the B
+//     operands of the dQ product and written to an LDS exchange buffer;
+//   role dQ (waves 4-7): one step later, once the step barrier has published that dS,
+//     dQ^T += K^T dS^T.
+// Role P holds the group's Q and dO columns, role dQ the dQ accumulator (96 registers a
+// lane), so two waves fit a SIMD, all eight waves have queries at 192-token blocks, and
+// each K/V tile is loaded once per block.  The roles run 48 and 24 products a step, and
+// all the vector work is role P's: role dQ's step is its LDS reads (the exchange and the
+// transposing K reads) and its products.  The K tile is read row-wise and transposed
+// (swizzle swz16); the V tile only row-wise (same swizzle).  Stages as in the split dK/dV
+// kernel: the K tile of tile t is read at steps t and t+1, step t refills the stage of
+// tile t-2 with tile t+2.
 // TOK: token-granular selection; role P keeps P only at the list positions its query
 // selected (the query's row of the list-position mask, two words cached per sub-tile and
 // refetched when a tile moves into another 32-position window).
@@ -846,13 +850,13 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   static_assert(LPW == 1, "one row group per wave");
   constexpr int NS = 4;                      // pipeline stages
   constexpr int PER_TILE = 2 * LPW;          // loads per wave per tile
-  constexpr int XF = 2 * M * 4 * 64;         // values of P one query group passes a tile
+  constexpr int XF = 2 * M * 4 * 64;         // values of dS one query group passes a tile
 
   __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage2[2 * TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char stage3[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][NQG][XF / 2];   // P, fp16 pairs
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2][NQG][XF / 2];   // dS, bf16 pairs
   __shared__ int32_t cols[DENSE ? 1 : kMaxBlocks];
   __shared__ int32_t offtab[TAB ? kOffsetTable : 1];
   __shared__ int32_t scratch[NW];
@@ -915,7 +919,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   }
   const int ntiles = __builtin_amdgcn_readfirstlane((nkeys + KT - 1) / KT);
 
-  // this lane's query in each sub-tile; Q (role P) or dO (role dQ) fragments in registers
+  // this lane's query in each sub-tile (role P holds its Q and dO fragments)
   const int qlim = DENSE ? g.L : g.S;
   const int qbase = qt * QT + qg * QW;
   const bool wave_busy = qbase < qlim;   // otherwise: loads and barriers only
@@ -924,19 +928,6 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
     const int rqc = rq < qlim ? rq : 0;
     return DENSE ? rqc : block_base(g, iblk) + block_offset(g, rqc);
   };
-  const uint16_t* __restrict__ QO = role_p ? Q : dO;
-  bf16x8 qof[M][D / 32];
-  float rowv[M];   // lse * log2(e) (role P) or delta (role dQ) of this lane's queries
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int32_t x = query_token(m);
-    const int32_t qoff = row_offset(g, grp, x);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      qof[m][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(QO + qoff + s * 32 + g16 * 8));
-    rowv[m] = role_p ? a.lse[size_t(grp) * g.L + x] * kLog2e
-                     : a.delta[size_t(grp) * g.L + x];
-  }
 
   // loader: one instruction moves 4 rows; lane L fills row L/16 at chunk position L % 16
   const int32_t hstride = g.Hh * D;
@@ -990,16 +981,15 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   const float c2 = a.scale_log2;
 
   using Acc = f32x4[2][M];
-  // S^T = K Q^T (role P, rows of the K tile) or dP^T = V dO^T (role dQ, rows of V)
-  auto products = [&](const unsigned char* rows, Acc& sacc, bool minus_row)
+  using Frag = bf16x8[M][D / 32];
+  // S^T = K Q^T (rows of the K tile, B = Q) or dP^T = V dO^T (rows of the V tile, B = dO),
+  // the accumulator of key sub-tile ks and query sub-tile m starting at init[ks][m]
+  auto products = [&](const unsigned char* rows, const Frag& bf, Acc& sacc, const Acc& init)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const float c = minus_row ? -rowv[m] : 0.f;
-        sacc[ks][m] = f32x4{c, c, c, c};
-      }
+      for (int m = 0; m < M; ++m) sacc[ks][m] = init[ks][m];
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
 #pragma unroll
@@ -1008,7 +998,7 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
             rows + ks * 16 * ROWB + roff[s]));
 #pragma unroll
         for (int m = 0; m < M; ++m)
-          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, qof[m][s], sacc[ks][m],
+          sacc[ks][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra, bf[m][s], sacc[ks][m],
                                                                 0, 0, 0);
       }
   };
@@ -1018,15 +1008,33 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
     for (int m = 0; m < M; ++m)
       pm[m].init(a.posmask + size_t(grp * g.L + query_token(m)) * a.mwords, a.mwords);
   }
-  // role P, tile t in stage sb: P to the exchange buffer (keys past the end, and with TOK
-  // unselected list positions: P = 0, by a select since an empty row has lse = -inf)
-  auto step_p = [&](const unsigned char* sb, uint32_t* xb, int t, Acc& sacc)
+  // role P, tile t in stage sb: S and dP, then dS = P (dP - delta) packed as the B operands
+  // of dQ^T += K^T dS^T, to the exchange buffer (keys past the end, and with TOK unselected
+  // list positions: P = 0, by a select since an empty row has lse = -inf, and so dS = 0)
+  auto step_p = [&](const unsigned char* sb, uint32_t* xb, int t, const Frag& qf,
+                    const Frag& df, const float (&lse2)[M], const float (&ndl)[M])
       __attribute__((always_inline)) {
-    products(sb, sacc, false);
-    const bool ragged = t * KT + KT > nkeys;   // uniform
-    // TOK: the launcher takes this kernel only for blocks of more than 128 tokens, so the
-    // tile's keys lie at list positions li0 (offsets below the boundary) and li0 + 1: two
-    // mask bits a query, and one compare a key
+    // S starts at -inf for the keys past the end of the ragged last tile (never with ALN:
+    // the stream is a multiple of the tile), so that their P is 0; dP starts at -delta
+    Acc s0, d0;
+    float kb[2][4] = {};
+    if (!ALN && t * KT + KT > nkeys) {   // uniform
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kb[ks][i] = t * KT + ks * 16 + 4 * g16 + i >= nkeys ? -INFINITY : 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        s0[ks][m] = f32x4{kb[ks][0], kb[ks][1], kb[ks][2], kb[ks][3]};
+        d0[ks][m] = f32x4{ndl[m], ndl[m], ndl[m], ndl[m]};
+      }
+    Acc sacc, dacc;
+    products(sb, qf, sacc, s0);
+    products(sb + TILE, df, dacc, d0);   // dP^T - delta
     bool b0[TOK ? M : 1], b1[TOK ? M : 1];
     int bh = 0;   // the boundary, counted from this lane's first key
     if constexpr (TOK) {
@@ -1046,49 +1054,29 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
       for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[ks][m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -rowv[m]));
+          pv[ks][m][i] = __builtin_amdgcn_exp2f(fmaf(sacc[ks][m][i], c2, -lse2[m]));
           if constexpr (TOK) pv[ks][m][i] = ((ks * 16 + i) < bh ? b0[m] : b1[m]) ? pv[ks][m][i] : 0.f;
         }
-    // the ragged last tile only (a uniform branch, so the other tiles pay no selects)
-    if (ragged) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (t * KT + ks * 16 + 4 * g16 + i >= nkeys) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) pv[ks][m][i] = 0.f;
-          }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      *reinterpret_cast<u32x4*>(xb + (m * 64 + lane) * 4) =
-          u32x4{pack_f16x2(pv[0][m][0], pv[0][m][1]), pack_f16x2(pv[0][m][2], pv[0][m][3]),
-                pack_f16x2(pv[1][m][0], pv[1][m][1]), pack_f16x2(pv[1][m][2], pv[1][m][3])};
-  };
-  // role dQ: dS^T of the previous tile (P in xb, dP in dprev), packed as B operands
-  auto finish_ds = [&](const uint32_t* xb, const Acc& dprev, bf16x8 (&sbf)[M])
-      __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      float sv[2][4];
-      const u32x4 p4 = *reinterpret_cast<const u32x4*>(xb + (m * 64 + lane) * 4);
+      float d[2][4];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)   // P (dP - delta)
-          sv[ks][i] = mul_f16(p4[2 * ks + (i >> 1)], i & 1, dprev[ks][m][i]);
-      sbf[m] = as_bf16x8(u32x4{pack_bf16x2(sv[0][0], sv[0][1]), pack_bf16x2(sv[0][2], sv[0][3]),
-                               pack_bf16x2(sv[1][0], sv[1][1]), pack_bf16x2(sv[1][2], sv[1][3])});
+        for (int i = 0; i < 4; ++i) d[ks][i] = pv[ks][m][i] * dacc[ks][m][i];
+      *reinterpret_cast<u32x4*>(xb + (m * 64 + lane) * 4) =
+          u32x4{pack_bf16x2(d[0][0], d[0][1]), pack_bf16x2(d[0][2], d[0][3]),
+                pack_bf16x2(d[1][0], d[1][1]), pack_bf16x2(d[1][2], d[1][3])};
     }
+  };
+  // role dQ: the packed dS of a tile from the exchange buffer
+  auto read_ds = [&](const uint32_t* xb, bf16x8 (&sbf)[M]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      sbf[m] = as_bf16x8(*reinterpret_cast<const u32x4*>(xb + (m * 64 + lane) * 4));
   };
 
   int32_t noff;
-  Acc dprev;   // role dQ: dP^T of the previous tile (role P: its S^T)
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int m = 0; m < M; ++m) dprev[ks][m] = f32x4{0.f, 0.f, 0.f, 0.f};
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -1097,6 +1085,23 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
   // both loops pass the same barriers
   auto run = [&](auto RPc) __attribute__((always_inline)) {
     constexpr bool RP = decltype(RPc)::value;
+    // role P: Q and dO fragments, lse * log2(e) and -delta of this lane's queries
+    Frag qf, df;
+    float lse2[M], ndl[M];
+    if constexpr (RP) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int32_t x = query_token(m);
+        const int32_t qoff = row_offset(g, grp, x);
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+          qf[m][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Q + qoff + s * 32 + g16 * 8));
+          df[m][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(dO + qoff + s * 32 + g16 * 8));
+        }
+        lse2[m] = a.lse[size_t(grp) * g.L + x] * kLog2e;
+        ndl[m] = -a.delta[size_t(grp) * g.L + x];
+      }
+    }
     f32x4 qacc[RP ? 1 : M][RP ? 1 : D / 16];   // role dQ: dQ^T
     if constexpr (!RP) {
 #pragma unroll
@@ -1129,15 +1134,11 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
       noff = tile_offsets(t + 3);
       if (wave_busy) {
         if constexpr (RP) {
-          step_p(stage(STc), &xbuf[ST & 1][qg][0], t, dprev);
-        } else {
-          // the previous tile first: its dP registers are free before this tile's dP
-          if (t > 0) {
-            bf16x8 sbf[M];
-            finish_ds(&xbuf[(ST + 1) & 1][qg][0], dprev, sbf);
-            accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
-          }
-          products(stage(STc) + TILE, dprev, true);   // dP^T - delta
+          step_p(stage(STc), &xbuf[ST & 1][qg][0], t, qf, df, lse2, ndl);
+        } else if (t > 0) {   // the previous tile's dS, posted by role P before this barrier
+          bf16x8 sbf[M];
+          read_ds(&xbuf[(ST + 1) & 1][qg][0], sbf);
+          accumulate(stage(std::integral_constant<int, ST + NS - 1>{}), sbf);
         }
       }
     };
@@ -1154,14 +1155,14 @@ void attn_bwd_dq_split_bf16_kernel(AttnParams a) {
     if (t < ntiles) step(I0{}, t);
     if (t + 1 < ntiles) step(I1{}, t + 1);
     if (t + 2 < ntiles) step(I2{}, t + 2);
-    // role dQ: the dS and dQ^T of the last tile, once its P is published
+    // role dQ: the dQ^T of the last tile, once its dS is published
     wait_vmcnt_lds<0>();   // also: the loads past the end land before the LDS is released
     __syncthreads();
     if constexpr (!RP) {
       if (wave_busy && ntiles > 0) {
         const int last = ntiles - 1;
         bf16x8 sbf[M];
-        finish_ds(&xbuf[last & 1][qg][0], dprev, sbf);
+        read_ds(&xbuf[last & 1][qg][0], sbf);
         switch (last & 3) {
           case 0: accumulate(stage0, sbf); break;
           case 1: accumulate(stage1, sbf); break;
@@ -1811,12 +1812,9 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128) {
     // 192 queries a workgroup (query groups of 48) when 192-query tiles pad a block no
-    // more than 128-query ones and 128-query tiles would leave more than an eighth of
-    // their query slots empty (192-token blocks: a quarter).  Its two roles are not
-    // balanced (role P has half the products of role dQ), which costs more than the
-    // empty slots save on long blocks.
+    // more than 128-query ones (the rule of the forward and dK/dV)
     const int p128 = (lim + 127) / 128 * 128;
-    if ((lim + 191) / 192 * 192 <= p128 && (p128 - lim) * 8 > p128) {
+    if ((lim + 191) / 192 * 192 <= p128) {
       // (this implies lim > 128, as the token instance's two-position key tiles need)
       launch_dq_split_bf16<DENSE, GT, TOK>(a, s);
       return;

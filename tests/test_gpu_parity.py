@@ -38,8 +38,8 @@ CASES = [
     # d = 128, 192-token blocks, two batch entries: the split dK/dV and dQ kernels over
     # head groups of both
     ("small3d_192_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.8, "bf16", 128, 2),
-    # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and dK/dV
-    # kernels, three 128-query tiles in dQ, and a block count that is no multiple of 8
+    # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and the split
+    # dK/dV and dQ kernels, and a block count that is no multiple of 8
     ("tiles2_3d_384", "l3d_55k", dict(T=8, H=36, W=16), LayerSpec(2, (4, 12, 8)), 0.6, "bf16", 128, 1),
     # 576 blocks of 8: above the block count up to which launches rank the lists
     ("unranked_576_blocks", "l3d_55k", dict(T=8, H=18, W=32), LayerSpec(2, (2, 2, 2)), 0.97, "bf16", 128, 1),
@@ -265,9 +265,11 @@ def test_tau_one_selects_all_and_equals_dense(dtype):
             assert max_err(to_np(t), r) <= tol
 
 
-def test_dense_natural_order_ragged_length():
-    # L = 3*10*11 = 330: not a multiple of any tile
-    p, inp = _small(lat=(3, 10, 11), block=(3, 10, 11), layer=2)
+# lengths that are no multiple of any tile: 330 takes the 48-query forward and the split
+# dK/dV and dQ kernels, 250 the 32-query ones
+@pytest.mark.parametrize("lat", [(3, 10, 11), (2, 5, 25)], ids=["L330", "L250"])
+def test_dense_natural_order_ragged_length(lat):
+    p, inp = _small(lat=lat, block=lat, layer=2)
     d = {x: inp[x].to(DEV) for x in ("q", "k", "v", "do")}
     o, lse = vmoba_dense_attn_fwd(p, d["q"], d["k"], d["v"])
     dq, dk, dv = vmoba_dense_attn_bwd(p, d["q"], d["k"], d["v"], o, lse, d["do"])
