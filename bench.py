@@ -174,11 +174,16 @@ def dkdv_kernel_name(klim, head_dim, bf16):
     return "attn_bwd_dkdv_bf16_kernel"
 
 
-def dq_kernel_name(qlim, head_dim, bf16):
+def dq_kernel_name(qlim, head_dim, bf16, rows):
     """The dQ kernel the library launches: 192 queries a workgroup in query groups of 48,
     each split over two waves, at d = 128 when 192-query tiles pad no more than 128-query
-    ones."""
-    if bf16 and head_dim == 128 and -(-qlim // 192) * 192 <= -(-qlim // 128) * 128:
+    ones and either 128-query tiles would leave more than an eighth of their slots empty or
+    the launch has at least 1,024 such workgroups (`rows`: head groups times query
+    blocks)."""
+    p128 = -(-qlim // 128) * 128
+    t192 = -(-qlim // 192)
+    if (bf16 and head_dim == 128 and t192 * 192 <= p128
+            and ((p128 - qlim) * 8 > p128 or rows * t192 >= 1024)):
         return "attn_bwd_dq_split_bf16_kernel"
     return "attn_bwd_dq_bf16_kernel"
 
@@ -312,7 +317,7 @@ def run_config(workload, layer, tau, steps, warmup, dense_reps, cpu_sample,
     select_bytes = 2.0 * p.groups * nb * d * 4 + 6.0 * p.groups * nb * nb * 4
     kernel_names = {"fwd": fwd_kernel_name(S, d, dtype == torch.bfloat16),
                     "dkdv": dkdv_kernel_name(S, d, dtype == torch.bfloat16),
-                    "dq": dq_kernel_name(S, d, dtype == torch.bfloat16)}
+                    "dq": dq_kernel_name(S, d, dtype == torch.bfloat16, p.groups * nb)}
 
     dense = None
     if dense_reps > 0:

@@ -1812,9 +1812,14 @@ static void launch_dq_bf16(AttnParams a, hipStream_t s) {
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128) {
     // 192 queries a workgroup (query groups of 48) when 192-query tiles pad a block no
-    // more than 128-query ones (the rule of the forward and dK/dV)
+    // more than 128-query ones (the rule of the forward and dK/dV), and either 128-query
+    // tiles would leave more than an eighth of their query slots empty or the launch has
+    // at least 1,024 of these workgroups (four rounds at one a CU): with fewer, the
+    // 32-query kernel's smaller workgroups (two a CU) end the launch sooner
     const int p128 = (lim + 127) / 128 * 128;
-    if ((lim + 191) / 192 * 192 <= p128) {
+    const int t192 = (lim + 191) / 192;
+    const long wgs = long(g.B) * g.Hh * (DENSE ? 1 : g.Nb) * t192;
+    if (t192 * 192 <= p128 && ((p128 - lim) * 8 > p128 || wgs >= 1024)) {
       // (this implies lim > 128, as the token instance's two-position key tiles need)
       launch_dq_split_bf16<DENSE, GT, TOK>(a, s);
       return;

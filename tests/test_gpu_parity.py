@@ -38,8 +38,9 @@ CASES = [
     # d = 128, 192-token blocks, two batch entries: the split dK/dV and dQ kernels over
     # head groups of both
     ("small3d_192_b2", "l3d_55k", dict(T=8, H=12, W=16), LayerSpec(2, (4, 6, 8)), 0.8, "bf16", 128, 2),
-    # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and the split
-    # dK/dV and dQ kernels, and a block count that is no multiple of 8
+    # 12 blocks of 384: two 192-row tiles per block in the 48-wide forward and dK/dV
+    # kernels, three 128-query tiles in dQ (a launch this small keeps the 32-query dQ),
+    # and a block count that is no multiple of 8
     ("tiles2_3d_384", "l3d_55k", dict(T=8, H=36, W=16), LayerSpec(2, (4, 12, 8)), 0.6, "bf16", 128, 1),
     # 576 blocks of 8: above the block count up to which launches rank the lists
     ("unranked_576_blocks", "l3d_55k", dict(T=8, H=18, W=32), LayerSpec(2, (2, 2, 2)), 0.97, "bf16", 128, 1),
