@@ -317,6 +317,56 @@ def test_caller_lists_with_empty_row_and_bad_entries():
     assert np.all(np.isneginf(ln[0, 1, empty_tok]))
 
 
+def _append_bad_entry(ptr, idx, g, row, bad):
+    """A copy of one head group's CSR (or CSC) with an out-of-range entry appended to one
+    row (entries after it shift by one)."""
+    ptr2, idx2 = ptr.clone(), idx.clone()
+    end = int(ptr[g, row + 1])
+    idx2[g, end + 1:] = idx[g, end:-1]
+    idx2[g, end] = bad
+    ptr2[g, row + 1:] += 1
+    return ptr2, idx2
+
+
+# 96-token blocks take the 32-wide kernels, 192-token blocks the 48-wide forward and the
+# split dK/dV and dQ kernels
+@pytest.mark.parametrize("lat,block", [((4, 12, 16), (2, 6, 8)), ((8, 12, 16), (4, 6, 8))],
+                         ids=["S96", "S192"])
+def test_caller_lists_backward_with_empty_row_and_bad_entries(lat, block):
+    p, inp = _small(heads=2, lat=lat, block=block)
+    nb = (lat[0] // block[0]) * (lat[1] // block[1]) * (lat[2] // block[2])
+    mem = oracle.block_members(p.T, p.H, p.W, p.block)
+    empty_tok = mem[3]
+    # the empty row's queries get no upstream gradient: they then add nothing to dK and dV
+    # and have dQ = 0, as the oracle's gradients with that row given its diagonal do too
+    inp = dict(inp)
+    do = inp["do"].clone()
+    do[0, torch.as_tensor(empty_tok, dtype=torch.long), 1] = 0
+    inp["do"] = do
+    d = {x: inp[x].to(DEV) for x in ("q", "k", "v", "do")}
+    rng = np.random.default_rng(1)
+    mask = rng.random((1, 2, nb, nb)) < 0.4
+    mask[0, :, np.arange(nb), np.arange(nb)] = True
+    mask[0, 1, 3, :] = False          # an empty query row
+    rp, ci, cp, ri = (t.cpu() for t in csr_to_device(mask, "cpu"))
+    rp2, ci2 = _append_bad_entry(rp, ci, 0, 0, nb + 5)
+    cp2, ri2 = _append_bad_entry(cp, ri, 0, 1, -7)
+    o, lse = vmoba_sparse_attn_fwd(p, d["q"], d["k"], d["v"], rp2.to(DEV), ci2.to(DEV))
+    dq, dk, dv = vmoba_sparse_attn_bwd(p, d["q"], d["k"], d["v"], o, lse, d["do"],
+                                       rp2.to(DEV), ci2.to(DEV), cp2.to(DEV), ri2.to(DEV))
+    torch.cuda.synchronize()
+    qn, kn, vn, dn = (to_np(inp[x]) for x in ("q", "k", "v", "do"))
+    m2 = mask.copy()
+    m2[0, 1, 3, 3] = True
+    o_ref, lse_ref = oracle.sparse_attention_fwd(qn, kn, vn, mem, m2)
+    g_ref = oracle.sparse_attention_bwd(qn, kn, vn, o_ref, lse_ref, dn, mem, m2)
+    for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), g_ref):
+        e = max_err(to_np(t), r)
+        print(f"{name} max-abs {e:.3g}")
+        assert e <= 2e-2, name
+    assert np.all(to_np(dq)[0, empty_tok, 1] == 0.0)
+
+
 def test_maximum_block_count_selection():
     # 1024 one-token blocks: the largest pool the selection accepts (1,048,576 pairs)
     p, inp = _small(heads=1, lat=(1, 32, 32), block=(1, 1, 1), layer=2)
