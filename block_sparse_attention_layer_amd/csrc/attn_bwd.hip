@@ -373,9 +373,11 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 }
 
 // ---------------------------------------------------------------------------------
-// dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16.  A workgroup covers 192 keys (a whole
-// 192-token block) in four key groups of 48 keys (three 16-key sub-tiles), so every Q /
-// dO fragment a wave reads from LDS feeds three products.
+// dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16.  A workgroup covers four key groups of
+// 16*KS keys: with KS = 3, 192 keys (a whole 192-token block) in groups of 48, so every Q /
+// dO fragment a wave reads from LDS feeds three products; with KS = 2, 128 keys in groups
+// of 32 (two products a fragment), for blocks that 192-key tiles would pad more than
+// 128-key ones (216-, 504-, 1,560-token blocks).  The description below is for KS = 3.
 //
 // Per 32-query tile and key group:
 //   S = Q K^T and dP = dO V^T as 2 query sub-tiles x 3 key sub-tiles x 4 d-steps (A = Q or
@@ -417,11 +419,11 @@ __device__ __forceinline__ int swz16(int r) { return 2 * (r & 7); }
 // TOK: token-granular selection; role P keeps P only where the query token's key-block
 // mask has this block's bit (dS then vanishes with it).  Wave 2 loads the tile's mask
 // words into its slot instead of an LSE copy.
-template <bool DENSE, bool TAB, typename GT, bool TOK = false, bool ALN = false>
+template <bool DENSE, bool TAB, typename GT, bool TOK = false, bool ALN = false, int KS = 3>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_split_bf16_kernel(AttnParams a) {
   constexpr int D = 128, NW = 8, NT = 512, NKG = 4;
-  constexpr int KS = 3;                      // key sub-tiles per wave
+  // KS: key sub-tiles of 16 per wave
   constexpr int KW = 16 * KS;                // keys per key group
   constexpr int KWG = NKG * KW;              // keys per workgroup
   constexpr int QT = 32;                     // queries per tile
@@ -1753,19 +1755,20 @@ static void launch_delta(const Geom& g, const void* o, const void* dout, float* 
                                          static_cast<const T*>(dout), delta);
 }
 
-template <bool DENSE, typename GT, bool TOK = false>
+template <bool DENSE, typename GT, bool TOK = false, int KS = 3>
 static void launch_dkdv_split_bf16(AttnParams a, hipStream_t s) {
   const Geom& g = a.g;
   const int lim = DENSE ? g.L : g.S;
   const int rows = DENSE ? 1 : g.Nb;
-  a.tiles = (lim + 191) / 192;
+  constexpr int KWG = 4 * 16 * KS;   // keys a workgroup
+  a.tiles = (lim + KWG - 1) / KWG;
   const int grid = launch_grid<DENSE>(a, rows);
   if (!DENSE && g.S <= kOffsetTable && g.S % 32 == 0)
-    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK, !DENSE><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK, !DENSE, KS><<<grid, 512, 0, s>>>(a);
   else if (!DENSE && g.S <= kOffsetTable)
-    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, !DENSE, GT, TOK, false, KS><<<grid, 512, 0, s>>>(a);
   else
-    attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT, TOK><<<grid, 512, 0, s>>>(a);
+    attn_bwd_dkdv_split_bf16_kernel<DENSE, false, GT, TOK, false, KS><<<grid, 512, 0, s>>>(a);
 }
 
 template <int D, bool DENSE, typename GT, bool TOK = false>
@@ -1774,12 +1777,13 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128) {
-    // 192 keys a workgroup (key groups of 48) when 192-key tiles pad a block no more
-    // than 128-key ones
-    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
-      launch_dkdv_split_bf16<DENSE, GT, TOK>(a, s);
-      return;
-    }
+    // the split kernel: 192 keys a workgroup (key groups of 48) when 192-key tiles pad a
+    // block no more than 128-key ones, else 128 keys a workgroup (key groups of 32)
+    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128)
+      launch_dkdv_split_bf16<DENSE, GT, TOK, 3>(a, s);
+    else
+      launch_dkdv_split_bf16<DENSE, GT, TOK, 2>(a, s);
+    return;
   }
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
