@@ -166,10 +166,10 @@ def fwd_kernel_name(qlim, head_dim, bf16):
 
 
 def dkdv_kernel_name(klim, head_dim, bf16):
-    """The dK/dV kernel the library launches: at d = 128 the split kernel (key groups of 48,
-    or of 32 where 192-key tiles would pad more than 128-key ones, each group split over two
-    waves on 16x16x32 MFMA), else the 32-key kernel."""
-    if bf16 and head_dim == 128:
+    """The dK/dV kernel the library launches: 192 keys a workgroup in key groups of 48, each
+    split over two waves (16x16x32 MFMA), at d = 128 when 192-key tiles pad no more than
+    128-key ones."""
+    if bf16 and head_dim == 128 and -(-klim // 192) * 192 <= -(-klim // 128) * 128:
         return "attn_bwd_dkdv_split_bf16_kernel"
     return "attn_bwd_dkdv_bf16_kernel"
 

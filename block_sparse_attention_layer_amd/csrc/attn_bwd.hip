@@ -374,10 +374,8 @@ void attn_bwd_dkdv_bf16_kernel(AttnParams a) {
 
 // ---------------------------------------------------------------------------------
 // dK, dV for d = 128 on v_mfma_f32_16x16x32_bf16.  A workgroup covers four key groups of
-// 16*KS keys: with KS = 3, 192 keys (a whole 192-token block) in groups of 48, so every Q /
-// dO fragment a wave reads from LDS feeds three products; with KS = 2, 128 keys in groups
-// of 32 (two products a fragment), for blocks that 192-key tiles would pad more than
-// 128-key ones (216-, 504-, 1,560-token blocks).  The description below is for KS = 3.
+// 16*KS keys; as launched (KS = 3), 192 keys (a whole 192-token block) in groups of 48, so
+// every Q / dO fragment a wave reads from LDS feeds three products.
 //
 // Per 32-query tile and key group:
 //   S = Q K^T and dP = dO V^T as 2 query sub-tiles x 3 key sub-tiles x 4 d-steps (A = Q or
@@ -1777,13 +1775,13 @@ static void launch_dkdv_bf16(AttnParams a, hipStream_t s) {
   constexpr int NWK = 4;
   const int lim = DENSE ? g.L : g.S;
   if constexpr (D == 128) {
-    // the split kernel: 192 keys a workgroup (key groups of 48) when 192-key tiles pad a
-    // block no more than 128-key ones, else 128 keys a workgroup (key groups of 32)
-    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128)
+    // 192 keys a workgroup (key groups of 48) when 192-key tiles pad a block no more
+    // than 128-key ones.  (The same kernel with key groups of 32 for the other blocks
+    // measured no faster than this 32-key kernel inside a whole step.)
+    if ((lim + 191) / 192 * 192 <= (lim + 127) / 128 * 128) {
       launch_dkdv_split_bf16<DENSE, GT, TOK, 3>(a, s);
-    else
-      launch_dkdv_split_bf16<DENSE, GT, TOK, 2>(a, s);
-    return;
+      return;
+    }
   }
   const int rows = DENSE ? 1 : g.Nb;
   a.tiles = (lim + NWK * 32 - 1) / (NWK * 32);
